@@ -1,0 +1,104 @@
+/*
+ * synth_gpu.hip -- seeded synthetic inputs on the GPU, plus the plain copy
+ * kernel used to calibrate HBM traffic counters and the practical copy
+ * ceiling.  Holds none of the optimizer step's arithmetic.
+ *
+ * The generator is the same definition as synth_cpu.c, implemented
+ * independently here:
+ *   SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): output n of the stream
+ *   seeded with `key` is mix(key + (n+1)*0x9e3779b97f4a7c15), mix being
+ *   z ^= z>>30; z *= 0xbf58476d1ce4e5b9; z ^= z>>27; z *= 0x94d049bb133111eb;
+ *   z ^= z>>31.  Element j sums the twelve 16-bit fields of outputs 3j..3j+2
+ *   (Irwin-Hall(12)): z = (2*sum - 786420) * 2^-17, exact in integers and
+ *   exactly representable in binary32; value = z * sigma (one rounding),
+ *   then rounded to nearest-even into the storage format.
+ */
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t kGamma = 0x9e3779b97f4a7c15ull;
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ float unit_variate(uint64_t key, uint64_t j) {
+    int64_t s = 0;
+#pragma unroll
+    for (uint64_t r = 0; r < 3; ++r) {
+        const uint64_t h = mix64(key + (3u * j + r + 1u) * kGamma);
+        s += (int64_t)(h & 0xffffu) + (int64_t)((h >> 16) & 0xffffu) +
+             (int64_t)((h >> 32) & 0xffffu) + (int64_t)(h >> 48);
+    }
+    const int32_t zi = (int32_t)(2 * s - 12 * 65535);
+    return (float)zi * 0x1p-17f;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) fill_normal(uint64_t key, int64_t start, int64_t n,
+                                                   float sigma, T* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float x = unit_variate(key, (uint64_t)(start + i)) * sigma;
+        out[i] = static_cast<T>(x); /* round to nearest even */
+    }
+}
+
+/* Plain streaming copy of 16-byte words: the reference kernel whose
+ * FETCH_SIZE/WRITE_SIZE per byte calibrate the counters and whose time is
+ * the practical read+write ceiling. */
+__global__ void __launch_bounds__(256) copy16(const uint4* __restrict__ src,
+                                              uint4* __restrict__ dst, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+}
+
+int grid_for(int64_t n) {
+    int64_t g = (n + 255) / 256;
+    if (g > 8192) g = 8192;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+}  // namespace
+
+extern "C" {
+
+/* dtype: 0 = fp32, 1 = fp16, 2 = bf16.  Returns 0 or a hipError_t. */
+int synth_fill_normal(uint64_t key, int64_t start, int64_t n, float sigma, void* out,
+                      int32_t dtype, void* stream) {
+    if (n <= 0) return 0;
+    hipStream_t s = (hipStream_t)stream;
+    const int g = grid_for(n);
+    if (dtype == 0)
+        hipLaunchKernelGGL(fill_normal<float>, dim3(g), dim3(256), 0, s, key, start, n, sigma,
+                           (float*)out);
+    else if (dtype == 1)
+        hipLaunchKernelGGL(fill_normal<_Float16>, dim3(g), dim3(256), 0, s, key, start, n,
+                           sigma, (_Float16*)out);
+    else if (dtype == 2)
+        hipLaunchKernelGGL(fill_normal<__bf16>, dim3(g), dim3(256), 0, s, key, start, n, sigma,
+                           (__bf16*)out);
+    else
+        return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+}
+
+/* nbytes must be a multiple of 16 and both pointers 16-byte aligned. */
+int synth_copy(const void* src, void* dst, int64_t nbytes, int32_t grid, void* stream) {
+    if (nbytes <= 0) return 0;
+    if ((nbytes & 15) || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
+        return (int)hipErrorInvalidValue;
+    const int64_t n16 = nbytes / 16;
+    const int g = grid > 0 ? grid : grid_for(n16);
+    hipLaunchKernelGGL(copy16, dim3(g), dim3(256), 0, (hipStream_t)stream, (const uint4*)src,
+                       (uint4*)dst, n16);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -1,0 +1,397 @@
+"""Pins of the oracle's optimizer-step arithmetic against what the pages and
+mathematics fix: exact rational arithmetic, closed forms, special cases,
+brute force and invariants (none re-types the oracle's own formula in float32).
+
+Pages: "DeepSpeed 与 FSDP" (docs.ifdog.com) -- ZeRO-2 Reduce-Scatter, ZeRO-Offload
+Adam equations, ZeRO++ INT8, the numpy 4-rank simulation; "PyTorch FSDP 源码级
+深度解析" (tbr8.org) §3.3 reduce_scatter AVG/SUM, §7.2 fp32 master; ZeRO reading
+at 2kiu.com §5.1 (AdamW lr 3e-5, betas (0.9, 0.999), eps 1e-8, wd 0.01, fp16
+dynamic scale 2^16 window 1000, clipping 1.0), §5.2 (ZeRO = DDP), §5.3
+(overflow and clipping consistency).
+"""
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction as Fr
+
+import numpy as np
+import pytest
+
+getcontext().prec = 60
+
+HP = dict(lr=3e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=1.0)
+
+
+def f16(x):
+    return np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+def bf16_bits(v):
+    return np.array([np.float32(v).view(np.uint32) >> 16], np.uint16)
+
+
+def nearest_f32(q: Fr) -> float:
+    """Exact round-to-nearest-even of a rational to binary32 (normal range)."""
+    c = np.float32(float(q))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        d = abs(Fr(float(cand)) - q)
+        if best is None or d < best[0] or (d == best[0] and (cand.view(np.uint32) & 1) == 0):
+            best = (d, cand)
+    return float(best[1])
+
+
+# ------------------------------------------------------------------ reduce
+def test_reduce_sum_of_copies_is_n_times(orc):
+    rng = np.random.default_rng(1)
+    x = f16(rng.standard_normal(777) * 1e-3)
+    for n in (1, 2, 3, 4, 8, 64):
+        red = orc.reduce([x] * n, orc.F16, 0, x.size, orc.SUM)
+        # n * x is exact in binary32 for an 11-bit significand and n <= 64
+        assert np.array_equal(red, orc.to_f32(x, orc.F16) * np.float32(n))
+        avg = orc.reduce([x] * n, orc.F16, 0, x.size, orc.AVG)
+        assert np.array_equal(avg.view(np.uint32), orc.to_f32(x, orc.F16).view(np.uint32))
+
+
+def test_reduce_scatter_equals_sum_then_split(orc):
+    """numpy simulation: summed_grad = sum(grads); grad_shards = split(summed)."""
+    rng = np.random.default_rng(2)
+    n_ranks, total = 4, 1001
+    shard = -(-total // n_ranks)
+    bufs = [f16(np.concatenate([rng.standard_normal(total) * 1e-3, np.zeros(shard * n_ranks - total)]))
+            for _ in range(n_ranks)]
+    exact = sum(orc.to_f32(b, orc.F16).astype(np.float64) for b in bufs)  # exact in float64
+    for r in range(n_ranks):
+        red = orc.reduce(bufs, orc.F16, r * shard, shard, orc.SUM)
+        # fp16 addends of this range sum exactly in binary32 as well
+        assert np.array_equal(red, exact[r * shard:(r + 1) * shard].astype(np.float32))
+
+
+def test_reduce_is_rank_ordered(orc):
+    """bf16 addends 2^24, 1, 1: rank order gives (2^24 + 1) -> 2^24 (tie to
+    even), then 2^24 again; any other order would give 2^24 + 2."""
+    bufs = [bf16_bits(2.0 ** 24), bf16_bits(1.0), bf16_bits(1.0)]
+    assert orc.reduce(bufs, orc.BF16, 0, 1, orc.SUM)[0] == 2.0 ** 24
+    assert orc.reduce(bufs[::-1], orc.BF16, 0, 1, orc.SUM)[0] == 2.0 ** 24 + 2
+
+
+def test_reduce_avg_is_a_true_division(orc):
+    """AVG = SUM / N rounded once: for N = 3 and sum 5 the result is the
+    binary32 nearest 5/3 (a product with fl(1/3) would round elsewhere)."""
+    bufs = [f16([2.0]), f16([2.0]), f16([1.0])]
+    red = orc.reduce(bufs, orc.F16, 0, 1, orc.AVG)[0]
+    assert red == nearest_f32(Fr(5, 3))
+    assert red != np.float32(5.0) * np.float32(1.0 / 3.0)
+
+
+# ------------------------------------------------------------------ overflow + norm
+def test_overflow_cases(orc):
+    rng = np.random.default_rng(4)
+    n_ranks, shard = 4, 64
+    base = [f16(rng.standard_normal(shard * n_ranks) * 1e-3) for _ in range(n_ranks)]
+
+    def ovf(bufs, r=1):
+        red = orc.reduce(bufs, orc.F16, r * shard, shard, orc.AVG)
+        return orc.unscale_stats(red, orc.F32, 65536.0)[1]
+
+    assert ovf(base) == 0
+    for val in (np.inf, -np.inf, np.nan):
+        b = [x.copy() for x in base]
+        b[2][shard + 17] = f16([val])[0]
+        assert ovf(b) == 1
+    b = [x.copy() for x in base]
+    b[0][shard + 5] = f16([np.inf])[0]
+    b[3][shard + 5] = f16([-np.inf])[0]            # inf + (-inf) = NaN
+    assert ovf(b) == 1
+    b = [x.copy() for x in base]
+    b[2][0] = f16([np.inf])[0]                     # outside rank 1's slice
+    assert ovf(b) == 0
+    # 65504 (largest fp16) summed over 4 ranks stays finite in fp32
+    b = [x.copy() for x in base]
+    for x in b:
+        x[shard + 3] = f16([65504.0])[0]
+    assert ovf(b) == 0
+
+
+def test_norm_constant_closed_form(orc):
+    """||u|| for n = k^2 copies of c, loss scale S: exactly k*|c|/S."""
+    for c, k, S in ((0.5, 3, 1.0), (-0.25, 40, 65536.0), (1.5, 100, 2.0 ** 10)):
+        g = np.full(k * k, c, np.float32)
+        s, o = orc.unscale_stats(g, orc.F32, S)
+        assert o == 0
+        assert s == (k * k) * (c / S) ** 2
+        assert math.sqrt(s) == k * abs(c) / S
+
+
+def test_norm_random_vs_correctly_rounded_sum(orc):
+    rng = np.random.default_rng(6)
+    for dt, scale in ((orc.F16, 65536.0), (orc.BF16, 1.0), (orc.F32, 2.0 ** 14)):
+        x = orc.from_f32(rng.standard_normal(50_000).astype(np.float32) * 1e-3, dt)
+        s, o = orc.unscale_stats(x, dt, scale)
+        u = orc.to_f32(x, dt).astype(np.float64) / scale        # exact: power-of-two scale
+        ref = math.fsum(float(a) * float(a) for a in u)           # correctly rounded
+        assert o == 0 and abs(s - ref) <= 1e-12 * ref
+
+
+def test_norm_accumulates_and_remote_terms(orc):
+    x = np.full(16, 2.0, np.float32)
+    s, o = orc.unscale_stats(x, orc.F32, 1.0, sumsq=10.0, overflow=0)
+    assert s == 10.0 + 64.0 and o == 0
+
+
+def test_clip_coef(orc):
+    assert orc.clip_coef(4.0, 1.0) == np.float32(1.0 / (2.0 + 1e-6))
+    assert orc.clip_coef(0.25, 1.0) == 1.0                 # 1/(0.5+1e-6) > 1
+    assert orc.clip_coef(1e6, 0.0) == 1.0                  # clipping off
+    assert orc.clip_coef(1e6, -1.0) == 1.0
+    assert orc.clip_coef(1089.0, 1.0) == np.float32(1.0 / (33.0 + 1e-6))
+
+
+# ------------------------------------------------------------------ AdamW
+def _fsqrt_fix(q):
+    d = (Decimal(q.numerator) / Decimal(q.denominator)).sqrt()
+    return Fr(d)
+
+
+def adamw_exact(u, p, m, v, coef, t, hp):
+    """The pages' Adam with bias correction plus decoupled weight decay, in
+    exact rational arithmetic (sqrt to 60 digits), hyper-parameters taken as
+    the exact decimals they are written as."""
+    b1, b2 = Fr(str(hp["beta1"])), Fr(str(hp["beta2"]))
+    lr, eps, wd = Fr(str(hp["lr"])), Fr(str(hp["eps"])), Fr(str(hp["weight_decay"]))
+    g = u * coef
+    m_t = b1 * m + (1 - b1) * g
+    v_t = b2 * v + (1 - b2) * g * g
+    mh = m_t / (1 - b1 ** t)
+    vh = v_t / (1 - b2 ** t)
+    p_t = p * (1 - lr * wd) - lr * mh / (_fsqrt_fix(vh) + eps)
+    return p_t, m_t, v_t
+
+
+def _rel(a, b):
+    return abs(Fr(float(a)) - b) / max(abs(b), Fr(1, 2 ** 126))
+
+
+@pytest.mark.parametrize("gdt,scale,max_norm,lr,wd", [
+    ("f16", 65536.0, 1.0, 3e-5, 0.01), ("bf16", 1.0, 1.0, 3e-5, 0.01),
+    ("f32", 1.0, 1e-3, 3e-5, 0.01), ("f16", 1024.0, 0.0, 3e-5, 0.01),
+    ("f16", 65536.0, 1.0, 1e-3, 0.1)])
+def test_adamw_three_steps_vs_exact_rational(orc, gdt, scale, max_norm, lr, wd):
+    """8 elements, 3 steps; each step starts from the oracle's own fp32 state
+    and is compared with the exact rational step (1e-6 relative).  Element
+    magnitudes span |u| ~ eps (the eps term matters) to |u| ~ 1e-2, and each
+    element's gradient keeps one sign so m carries no cancellation."""
+    code = {"f16": orc.F16, "bf16": orc.BF16, "f32": orc.F32}[gdt]
+    hp = dict(HP, max_grad_norm=max_norm, lr=lr, weight_decay=wd)
+    rng = np.random.default_rng(8)
+    sign = np.where(np.arange(8) % 2 == 0, 1.0, -1.0)
+    mags = np.array([1e-8, 3e-8, 1e-6, 1e-5, 1e-4, 1e-3, 5e-3, 1e-2])
+    p = (rng.standard_normal(8) * 0.02).astype(np.float32)
+    m = np.zeros(8, np.float32)
+    v = np.zeros(8, np.float32)
+    for t in (1, 2, 3):
+        u_target = sign * mags * (1.0 + 0.3 * rng.random(8))
+        g = orc.from_f32((u_target * scale).astype(np.float32), code)
+        u = [Fr(float(a)) / Fr(scale) for a in orc.to_f32(g, code)]
+        sumsq = sum(float(x) ** 2 for x in u)
+        coef = orc.clip_coef(sumsq, max_norm)
+        if max_norm > 0 and sumsq ** 0.5 > max_norm:
+            assert coef < 1.0
+        p0, m0, v0 = p.copy(), m.copy(), v.copy()
+        lp = orc.adamw(g, code, p, m, v, scale, coef, t, hp, orc.F16)
+        # the exact side uses the exact clip coefficient
+        c_ex = min(Fr(1), Fr(max_norm) / (_fsqrt_fix(sum(x * x for x in u)) + Fr(str(1e-6)))) \
+            if max_norm > 0 else Fr(1)
+        for i in range(8):
+            pe, me, ve = adamw_exact(u[i], Fr(float(p0[i])), Fr(float(m0[i])), Fr(float(v0[i])),
+                                     c_ex, t, hp)
+            assert _rel(p[i], pe) < 1e-6, ("p", t, i)
+            assert _rel(m[i], me) < 1e-6, ("m", t, i)
+            assert _rel(v[i], ve) < 1e-6, ("v", t, i)
+        # write-back is the fp16 rounding of the new master (numpy's cast)
+        assert np.array_equal(lp, p.astype(np.float16).view(np.uint16))
+
+
+def test_adamw_step1_closed_form(orc):
+    """t=1 with m=v=0: mh = g and vh = g^2, so the step is
+    p(1-lr*wd) - lr*g/(|g|+eps): for |g| >> eps about lr*sign(g)."""
+    g = np.array([1e-3, -2e-2, 5e-4, -7e-5], np.float32)
+    p = np.array([0.02, -0.01, 0.0, 0.5], np.float32)
+    m = np.zeros(4, np.float32)
+    v = np.zeros(4, np.float32)
+    p0 = p.copy()
+    orc.adamw(g, orc.F32, p, m, v, 1.0, 1.0, 1, HP)
+    expect = p0.astype(np.float64) * (1 - HP["lr"] * HP["weight_decay"]) \
+        - HP["lr"] * g / (np.abs(g) + HP["eps"])
+    assert np.allclose(p, expect, rtol=1e-6, atol=1e-12)
+    assert np.allclose(m, 0.1 * g, rtol=1e-6)
+    assert np.allclose(v, 0.001 * g.astype(np.float64) ** 2, rtol=1e-6)
+
+
+def test_adamw_special_cases(orc):
+    rng = np.random.default_rng(9)
+    n = 100
+    g = rng.standard_normal(n).astype(np.float32) * 1e-3
+    p = rng.standard_normal(n).astype(np.float32) * 0.02
+    m = rng.standard_normal(n).astype(np.float32) * 1e-4
+    v = np.abs(rng.standard_normal(n).astype(np.float32)) * 1e-7
+    # lr = 0 and wd = 0: the master does not move, bit for bit
+    pp, mm, vv = p.copy(), m.copy(), v.copy()
+    orc.adamw(g, orc.F32, pp, mm, vv, 1.0, 1.0, 5, dict(HP, lr=0.0, weight_decay=0.0))
+    assert np.array_equal(pp.view(np.uint32), p.view(np.uint32))
+    # zero gradient: only the decoupled decay acts, p' = p * fl(1 - lr*wd)
+    pp, mm, vv = p.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    orc.adamw(np.zeros(n, np.float32), orc.F32, pp, mm, vv, 1.0, 1.0, 1,
+              dict(HP, lr=1e-2, weight_decay=0.1))
+    assert np.array_equal(pp, p * np.float32(1.0 - 1e-2 * 0.1))
+    # beta1 = beta2 = 0: m' = g and v' = g*g exactly
+    pp, mm, vv = p.copy(), m.copy(), v.copy()
+    orc.adamw(g, orc.F32, pp, mm, vv, 1.0, 1.0, 3, dict(HP, beta1=0.0, beta2=0.0))
+    assert np.array_equal(mm, g) and np.array_equal(vv, g * g)
+    # padding (g = p = m = v = 0) stays exactly zero at every step
+    z = [np.zeros(16, np.float32) for _ in range(4)]
+    for t in range(1, 6):
+        lp = orc.adamw(z[0], orc.F32, z[1], z[2], z[3], 65536.0, 1.0, t, HP, orc.BF16)
+        assert not any(a.any() for a in z[1:]) and not lp.any()
+
+
+def test_zero_equals_ddp_on_oracle(orc):
+    """2kiu.com §5.2: with communication ignored ZeRO gives the same update
+    sequence as DDP.  The concatenation of N rank-shard steps (each rank's
+    norm = local + the other ranks' sums) equals one unsharded step over the
+    whole flat buffer, bit for bit, for 3 steps."""
+    rng = np.random.default_rng(10)
+    total = 1000
+    for n_ranks in (1, 2, 4, 8):
+        for max_norm in (1.0, 1e-6):
+            shard = -(-total // n_ranks)
+            padded = shard * n_ranks
+            p_full = np.zeros(padded, np.float32)
+            p_full[:total] = rng.standard_normal(total) * 0.02
+            m_full = np.zeros(padded, np.float32)
+            v_full = np.zeros(padded, np.float32)
+            ranks = [[p_full[r * shard:(r + 1) * shard].copy(), np.zeros(shard, np.float32),
+                      np.zeros(shard, np.float32)] for r in range(n_ranks)]
+            hp = dict(HP, max_grad_norm=max_norm)
+            sc_full = orc.make_scaler(65536.0, True)
+            sc_r = [orc.make_scaler(65536.0, True) for _ in range(n_ranks)]
+            for step in range(3):
+                bufs = []
+                for k in range(n_ranks):
+                    b = np.zeros(padded, np.float32)
+                    b[:total] = rng.standard_normal(total) * 1e-3
+                    bufs.append(f16(b))
+                red = orc.reduce(bufs, orc.F16, 0, padded, orc.AVG)
+                full = orc.shard_step(grad=red, grad_dtype=orc.F32, master=p_full,
+                                      exp_avg=m_full, exp_avg_sq=v_full, scaler=sc_full,
+                                      hp=hp, param_dtype=orc.F16)
+                reds = [orc.reduce(bufs, orc.F16, r * shard, shard, orc.AVG)
+                        for r in range(n_ranks)]
+                stats = [orc.unscale_stats(x, orc.F32, sc_r[r].loss_scale)
+                         for r, x in enumerate(reds)]
+                lps = []
+                for r in range(n_ranks):
+                    remote = sum(stats[k][0] for k in range(n_ranks) if k != r)
+                    out = orc.shard_step(grad=reds[r], grad_dtype=orc.F32, master=ranks[r][0],
+                                         exp_avg=ranks[r][1], exp_avg_sq=ranks[r][2],
+                                         scaler=sc_r[r], hp=hp, param_dtype=orc.F16,
+                                         remote_sumsq=remote)
+                    assert out["coef"] == full["coef"]
+                    lps.append(out["lp"])
+                assert np.array_equal(np.concatenate(lps), full["lp"])
+                for i, arr in enumerate((p_full, m_full, v_full)):
+                    cat = np.concatenate([ranks[r][i] for r in range(n_ranks)])
+                    assert np.array_equal(cat.view(np.uint32), arr.view(np.uint32))
+            # padding stayed zero
+            assert not p_full[total:].any()
+
+
+def test_skipped_step_leaves_state_untouched(orc):
+    rng = np.random.default_rng(12)
+    p = rng.standard_normal(64).astype(np.float32)
+    m = rng.standard_normal(64).astype(np.float32) * 1e-3
+    v = np.abs(rng.standard_normal(64).astype(np.float32)) * 1e-6
+    g = f16(rng.standard_normal(64) * 1e-3)
+    g[10] = f16([np.inf])[0]
+    sc = orc.make_scaler(65536.0, True)
+    before = [a.copy() for a in (p, m, v)]
+    res = orc.shard_step(grad=g, grad_dtype=orc.F16, master=p, exp_avg=m, exp_avg_sq=v,
+                         scaler=sc, hp=HP, param_dtype=orc.BF16, quant_block=256)
+    assert res["skipped"] == 1 and res["lp"] is None and res["q"] is None
+    for a, b in zip((p, m, v), before):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert sc.loss_scale == 32768.0 and sc.step == 0 and sc.good_steps == 0
+    # another rank's overflow skips this rank as well
+    g2 = f16(rng.standard_normal(64) * 1e-3)
+    res = orc.shard_step(grad=g2, grad_dtype=orc.F16, master=p, exp_avg=m, exp_avg_sq=v,
+                         scaler=sc, hp=HP, param_dtype=orc.BF16, remote_overflow=1)
+    assert res["skipped"] == 1 and sc.loss_scale == 16384.0
+
+
+# ------------------------------------------------------------------ loss scaler
+def test_scaler_sequence(orc):
+    sc = orc.make_scaler(2.0 ** 16, True, window=2)
+    table = []
+    for ovf in (0, 0, 0, 1, 0, 0, 1, 1, 0):
+        orc.scaler_update(sc, ovf)
+        table.append((sc.loss_scale, sc.good_steps, sc.step))
+    assert table == [(65536.0, 1, 1), (131072.0, 0, 2), (131072.0, 1, 3), (65536.0, 0, 3),
+                     (65536.0, 1, 4), (131072.0, 0, 5), (65536.0, 0, 5), (32768.0, 0, 5),
+                     (32768.0, 1, 6)]
+    floor = orc.make_scaler(2.0, True, window=1000, min_scale=1.0)
+    for _ in range(3):
+        orc.scaler_update(floor, 1)
+    assert floor.loss_scale == 1.0 and floor.step == 0
+    static = orc.make_scaler(65536.0, False)
+    for ovf in (0, 1, 0):
+        orc.scaler_update(static, ovf)
+    assert static.loss_scale == 65536.0 and static.step == 2
+    w1000 = orc.make_scaler(2.0 ** 16, True, window=1000)
+    for _ in range(999):
+        orc.scaler_update(w1000, 0)
+    assert w1000.loss_scale == 2.0 ** 16
+    orc.scaler_update(w1000, 0)
+    assert w1000.loss_scale == 2.0 ** 17 and w1000.step == 1000
+
+
+# ------------------------------------------------------------------ INT8
+def test_int8_closed_forms(orc):
+    blk = 256
+    for c in (0.75, -3.0e-3, 1.0 / 3.0):
+        x = f16(np.full(blk, c))
+        q, s = orc.quant_int8(x, orc.F16, blk)
+        cf = float(orc.to_f32(x[:1], orc.F16)[0])
+        assert np.all(q == (127 if cf > 0 else -127))
+        assert s[0] == np.float32(abs(np.float32(cf)) / np.float32(127.0))
+    q, s = orc.quant_int8(np.zeros(blk, np.uint16), orc.BF16, blk)
+    assert s[0] == 0.0 and not q.any()
+
+
+def test_int8_absmax_and_error_bound(orc):
+    rng = np.random.default_rng(13)
+    n = 256 * 7 + 93                                  # short last block
+    xf = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    for dt in (orc.F16, orc.BF16):
+        x = orc.from_f32(xf, dt)
+        q, s = orc.quant_int8(x, dt, 256)
+        assert s.size == -(-n // 256)
+        xv = orc.to_f32(x, dt)
+        for b in range(s.size):
+            seg = slice(b * 256, min((b + 1) * 256, n))
+            xs, qs = xv[seg], q[seg].astype(np.int32)
+            j = int(np.argmax(np.abs(xs)))
+            assert abs(qs[j]) == 127 and np.sign(qs[j]) == np.sign(xs[j])
+            err = np.abs(qs * np.float64(s[b]) - xs)
+            assert np.all(err <= s[b] * (0.5 + 2.0 ** -15))
+            assert np.all(np.abs(qs) <= 127)
+        # rounding is to nearest: no code is more than half a step off
+        assert np.all(np.abs(q.astype(np.float64) - xv / np.repeat(s, 256)[:n]) <= 0.5 + 1e-5)
+
+
+def test_int8_payload_halves_the_slot():
+    """2kiu.com §4.2: INT8 instead of 2-byte weights halves the All-Gather
+    volume; with one fp32 scale per 256 codes the payload is 50.78% of fp16."""
+    S = 1_093_750_000
+    nb = -(-S // 256)
+    assert nb == 4_272_461
+    assert S + 4 * nb == 1_110_839_844
+    assert abs((S + 4 * nb) / (2 * S) - (1 + 4 / 256) / 2) < 1e-6
