@@ -1,0 +1,262 @@
+"""Python binding of libzeroflat: one rank's sharded mixed-precision AdamW step
+over a FlatParameter on MI355X (gfx950).
+
+The functions mirror the C ABI in include/zeroflat.h one to one and only
+marshal arguments: torch tensors supply device pointers, the stream is torch's
+current HIP stream unless given, and every step runs in the library's
+kernels.  There is no fallback: importing this package fails if the library
+has not been built (``__graft_entry__.build()`` or ``python -m
+fsdp_sharded_mixed_flatparameter_amd._build``).
+"""
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzeroflat.so")
+
+ZERO_F32, ZERO_F16, ZERO_BF16 = 0, 1, 2
+ZERO_SUM, ZERO_AVG = 0, 1
+ZERO_STEP_FINALIZE = 1
+ZERO_MAX_RANKS = 256
+ZERO_MAX_PARTIALS = 2048
+
+EXPORTS = ("zero_last_error", "zero_flat_layout", "zero_step_state_init",
+           "zero_grad_reduce_shard", "zero_unscale_norm", "zero_adamw_shard_step",
+           "zero_quant_allgather_slot")
+
+
+class zero_span_t(C.Structure):
+    _fields_ = [("start", C.c_int64), ("end", C.c_int64)]
+
+
+class zero_segment_t(C.Structure):
+    _fields_ = [("param", C.c_int32), ("reserved", C.c_int32), ("off_in_param", C.c_int64),
+                ("off_in_shard", C.c_int64), ("len", C.c_int64)]
+
+
+class zero_layout_t(C.Structure):
+    _fields_ = [("total", C.c_int64), ("shard", C.c_int64), ("padded", C.c_int64),
+                ("pad", C.c_int64), ("n_ranks", C.c_int32), ("reserved", C.c_int32),
+                ("align", C.c_int64), ("bytes_dp", C.c_int64), ("bytes_z1", C.c_int64),
+                ("bytes_z2", C.c_int64), ("bytes_z3", C.c_int64)]
+
+
+class zero_step_state_t(C.Structure):
+    _fields_ = [("sumsq", C.c_double), ("overflow", C.c_int32),
+                ("remote_overflow", C.c_int32), ("remote_sumsq", C.c_double),
+                ("loss_scale", C.c_float), ("min_scale", C.c_float), ("dynamic", C.c_int32),
+                ("window", C.c_int32), ("good_steps", C.c_int32), ("step", C.c_int32),
+                ("beta1_pow", C.c_double), ("beta2_pow", C.c_double),
+                ("last_norm", C.c_double), ("last_coef", C.c_float),
+                ("last_skipped", C.c_int32), ("n_partials", C.c_int32),
+                ("reserved", C.c_int32), ("partials", C.c_double * ZERO_MAX_PARTIALS)]
+
+
+class zero_adamw_hparams_t(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("weight_decay", C.c_double),
+                ("max_grad_norm", C.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libzeroflat.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, u32 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32
+    L.zero_last_error.restype = C.c_char_p
+    L.zero_last_error.argtypes = []
+    L.zero_flat_layout.restype = C.c_int
+    L.zero_flat_layout.argtypes = [vp, i32, i32, i64, i32, i32, i32, i32, vp, vp, vp, i32, vp]
+    L.zero_step_state_init.restype = C.c_int
+    L.zero_step_state_init.argtypes = [vp, C.c_float, i32, i32, C.c_float]
+    L.zero_grad_reduce_shard.restype = C.c_int
+    L.zero_grad_reduce_shard.argtypes = [vp, i32, i32, i64, i64, i32, vp, vp, vp]
+    L.zero_unscale_norm.restype = C.c_int
+    L.zero_unscale_norm.argtypes = [vp, i32, i64, vp, vp]
+    L.zero_adamw_shard_step.restype = C.c_int
+    L.zero_adamw_shard_step.argtypes = [vp, i32, vp, vp, vp, i64, vp, i32, i64, vp, vp, i64,
+                                        i64, i32, vp, u32, vp, vp]
+    L.zero_quant_allgather_slot.restype = C.c_int
+    L.zero_quant_allgather_slot.argtypes = [vp, i32, i64, i32, vp, i64, vp, i64, vp]
+    return L
+
+
+_lib = _load()
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("libzeroflat error %d: %s" % (code, msg))
+        self.code = code
+
+
+def _check(rc):
+    if rc != 0:
+        raise ZeroError(rc, _lib.zero_last_error().decode())
+
+
+def lib():
+    return _lib
+
+
+def _dtype_code(t):
+    import torch
+    try:
+        return {torch.float32: ZERO_F32, torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16}[t.dtype]
+    except KeyError:
+        raise ValueError("unsupported dtype %s" % t.dtype) from None
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+def _contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+# ------------------------------------------------------------------ layout
+def zero_flat_layout(numels, n_ranks, align=1, param_bytes=2, grad_bytes=2, optim_bytes=12,
+                     rank=0):
+    """FlatParameter layout and per-rank accounting (host only)."""
+    n = len(numels)
+    arr = (C.c_int64 * max(n, 1))(*[int(x) for x in numels])
+    out = zero_layout_t()
+    spans = (zero_span_t * max(n, 1))()
+    cap = n + 1
+    segs = (zero_segment_t * cap)()
+    nseg = C.c_int32(0)
+    _check(_lib.zero_flat_layout(arr, n, n_ranks, align, param_bytes, grad_bytes, optim_bytes,
+                                 rank, C.byref(out), spans, segs, cap, C.byref(nseg)))
+    return dict(total=out.total, shard=out.shard, padded=out.padded, pad=out.pad,
+                n_ranks=out.n_ranks, align=out.align,
+                bytes=dict(dp=out.bytes_dp, z1=out.bytes_z1, z2=out.bytes_z2, z3=out.bytes_z3),
+                spans=[(spans[j].start, spans[j].end) for j in range(n)],
+                segments=[(segs[i].param, segs[i].off_in_param, segs[i].off_in_shard, segs[i].len)
+                          for i in range(nseg.value)])
+
+
+# ------------------------------------------------------------------ state
+STATE_BYTES = C.sizeof(zero_step_state_t)
+
+
+def zero_step_state_init(loss_scale, dynamic, window=1000, min_scale=1.0):
+    """Host zero_step_state_t for step 0 (ctypes struct)."""
+    st = zero_step_state_t()
+    _check(_lib.zero_step_state_init(C.byref(st), loss_scale, int(bool(dynamic)), window,
+                                     min_scale))
+    return st
+
+
+class StepState:
+    """Device-resident zero_step_state_t (a torch uint8 buffer) plus host views."""
+
+    def __init__(self, loss_scale, dynamic, window=1000, min_scale=1.0, device="cuda"):
+        import torch
+        self.buf = torch.empty(STATE_BYTES, dtype=torch.uint8, device=device)
+        self.upload(zero_step_state_init(loss_scale, dynamic, window, min_scale))
+
+    def upload(self, host_state):
+        import torch
+        raw = bytes(bytearray(host_state))
+        self.buf.copy_(torch.frombuffer(bytearray(raw), dtype=torch.uint8))
+
+    def read(self):
+        """Host copy of the state (synchronizes with the current stream)."""
+        raw = self.buf.cpu().numpy().tobytes()
+        return zero_step_state_t.from_buffer_copy(raw)
+
+    def set_remote(self, sumsq=0.0, overflow=0):
+        st = self.read()
+        st.remote_sumsq = float(sumsq)
+        st.remote_overflow = int(overflow)
+        self.upload(st)
+
+    def ptr(self):
+        return C.c_void_p(self.buf.data_ptr())
+
+
+def _state_ptr(state):
+    if state is None:
+        return None
+    return state.ptr() if isinstance(state, StepState) else C.c_void_p(state.data_ptr())
+
+
+# ------------------------------------------------------------------ the step
+def zero_grad_reduce_shard(grad_bufs, elem_offset, shard_numel, op, red_out, state=None,
+                           stream=None):
+    """red_out[i] = sum_k grad_bufs[k][elem_offset + i] (rank order), AVG -> / N;
+    accumulates the step statistics into `state` when given."""
+    if not grad_bufs:
+        raise ValueError("grad_bufs is empty")
+    dt = _dtype_code(grad_bufs[0])
+    for k, b in enumerate(grad_bufs):
+        _contig(b, "grad_bufs[%d]" % k)
+        if _dtype_code(b) != dt:
+            raise ValueError("grad_bufs dtypes differ")
+        if elem_offset + shard_numel > b.numel():
+            raise ValueError("grad_bufs[%d] is shorter than elem_offset + shard_numel" % k)
+    _contig(red_out, "red_out")
+    if red_out.dtype.itemsize != 4 or red_out.numel() < shard_numel:
+        raise ValueError("red_out must be float32 with >= shard_numel elements")
+    arr = (C.c_void_p * len(grad_bufs))(*[b.data_ptr() for b in grad_bufs])
+    _check(_lib.zero_grad_reduce_shard(arr, len(grad_bufs), dt, elem_offset, shard_numel, op,
+                                       _ptr(red_out), _state_ptr(state), _stream(stream)))
+
+
+def zero_unscale_norm(grad_shard, state, n=None, stream=None):
+    _contig(grad_shard, "grad_shard")
+    n = grad_shard.numel() if n is None else n
+    _check(_lib.zero_unscale_norm(_ptr(grad_shard), _dtype_code(grad_shard), n,
+                                  _state_ptr(state), _stream(stream)))
+
+
+def zero_adamw_shard_step(grad_shard, master, exp_avg, exp_avg_sq, allgather_buf, slot_offset,
+                          hp, state, q_buf=None, q_scales=None, q_slot_offset=0,
+                          q_scale_offset=0, q_block=256, finalize=True, stream=None):
+    """Skip-on-overflow, clip, AdamW on master/m/v, write-back into
+    allgather_buf[slot_offset:], optional INT8 payload, scaler update."""
+    n = master.numel()
+    for name, t in (("grad_shard", grad_shard), ("master", master), ("exp_avg", exp_avg),
+                    ("exp_avg_sq", exp_avg_sq), ("allgather_buf", allgather_buf)):
+        _contig(t, name)
+    if grad_shard.numel() < n or exp_avg.numel() != n or exp_avg_sq.numel() != n:
+        raise ValueError("shard tensors disagree in size")
+    if slot_offset + n > allgather_buf.numel():
+        raise ValueError("slot exceeds the all-gather buffer")
+    if q_buf is not None:
+        if q_slot_offset + n > q_buf.numel() or \
+                q_scale_offset + (n + q_block - 1) // q_block > q_scales.numel():
+            raise ValueError("INT8 slot exceeds its buffers")
+    h = hp if isinstance(hp, zero_adamw_hparams_t) else zero_adamw_hparams_t(**hp)
+    _check(_lib.zero_adamw_shard_step(
+        _ptr(grad_shard), _dtype_code(grad_shard), _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq),
+        n, _ptr(allgather_buf), _dtype_code(allgather_buf), slot_offset, _ptr(q_buf),
+        _ptr(q_scales), q_slot_offset, q_scale_offset, q_block, C.byref(h),
+        ZERO_STEP_FINALIZE if finalize else 0, _state_ptr(state), _stream(stream)))
+
+
+def zero_quant_allgather_slot(slot, q_buf, q_scales, q_slot_offset=0, q_scale_offset=0,
+                              block=256, n=None, stream=None):
+    _contig(slot, "slot")
+    n = slot.numel() if n is None else n
+    if q_slot_offset + n > q_buf.numel() or q_scale_offset + (n + block - 1) // block > q_scales.numel():
+        raise ValueError("INT8 slot exceeds its buffers")
+    _check(_lib.zero_quant_allgather_slot(_ptr(slot), _dtype_code(slot), n, block, _ptr(q_buf),
+                                          q_slot_offset, _ptr(q_scales), q_scale_offset,
+                                          _stream(stream)))
+
+
+from . import shard  # noqa: E402
+from .shard import ShardOptimizer  # noqa: E402,F401

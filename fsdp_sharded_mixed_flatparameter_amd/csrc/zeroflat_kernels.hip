@@ -1,0 +1,572 @@
+// zeroflat_kernels.hip -- gfx950 (MI355X, CDNA4, wave64) kernels of one
+// rank's sharded mixed-precision AdamW step over a FlatParameter.
+//
+// Every kernel here streams HBM once: none is a contraction, so there is no
+// MFMA work; the design goals are wide coalesced accesses, enough bytes in
+// flight per CU, and the per-element fp32 operation order fixed by the step's
+// definition (zeroflat.h), so results equal a plain IEEE evaluation bit for
+// bit.  Built with -ffp-contract=off (no FMA fusion) and correctly rounded
+// fp32 division and square root.
+//
+// Data mapping ("quad" tiles): a wavefront owns tiles of 256*kU consecutive
+// elements; in slice u of a tile, lane l holds elements 256u + 4l .. 4l+3, so
+// each fp32 array moves as one 16-byte access per lane (1 KiB per wave
+// instruction) and each 16-bit array as one 8-byte access.  One slice of 256
+// elements is exactly one INT8 block, reduced across the wave.  The reduce
+// kernel instead gives each lane 8 consecutive elements so its dominant
+// 16-bit reads are 16-byte accesses.  Tiles are assigned to waves grid-stride.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zf_launch.h"
+
+namespace zf {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kU = 2;                       // 256-element slices per adamw/quant tile
+constexpr int64_t kTile = 256 * kU;         // adamw/quant tile (elements per wave)
+constexpr int64_t kRTile = 512;             // reduce tile: 8 elements per lane
+constexpr int kMaxGridStep = 4096;          // adamw grid cap (blocks)
+constexpr int kMaxGridReduce = ZERO_MAX_PARTIALS;
+
+// ---------------------------------------------------------------- formats
+__device__ __forceinline__ float h2f(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float b2f(uint32_t h) { return __uint_as_float(h << 16); }
+// binary32 -> binary16 / bfloat16 rounding to nearest, ties to even, written
+// on the bit patterns so that no hardware conversion mode is involved.
+__device__ __forceinline__ uint32_t f2h(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    const uint32_t a = u & 0x7fffffffu;
+    uint32_t h;
+    if (a >= 0x7f800000u) {
+        h = a > 0x7f800000u ? 0x7e00u : 0x7c00u;           // quiet NaN / infinity
+    } else if (a >= 0x477ff000u) {
+        h = 0x7c00u;                                        // >= 65520 rounds to infinity
+    } else if (a >= 0x38800000u) {                          // normal binary16 (>= 2^-14)
+        const uint32_t m = a - 0x38000000u;                 // exponent bias 127 -> 15
+        h = (m + 0xfffu + ((m >> 13) & 1u)) >> 13;          // round at bit 13, ties to even
+    } else {                                                // subnormal binary16: quantum 2^-24,
+        h = __float_as_uint(__uint_as_float(a) + 0.5f) - 0x3f000000u;  // the ulp of 0.5
+    }
+    return sign | h;
+}
+__device__ __forceinline__ uint32_t f2b(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;  // quiet NaN
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;          // round at bit 16, ties to even
+}
+
+template <int DT>
+__device__ __forceinline__ float cvt16(uint32_t h) {
+    return DT == ZERO_F16 ? h2f(h) : b2f(h);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t round16(float x) {
+    return DT == ZERO_F16 ? f2h(x) : f2b(x);
+}
+
+template <int DT>
+__device__ __forceinline__ float load_one(const void* p, int64_t i) {
+    if constexpr (DT == ZERO_F32) return static_cast<const float*>(p)[i];
+    else return cvt16<DT>(static_cast<const uint16_t*>(p)[i]);
+}
+
+// four consecutive elements from a 16-byte (fp32) or 8-byte (16-bit) aligned address
+template <int DT>
+__device__ __forceinline__ void load_quad(const void* p, int64_t i, float out[4]) {
+    if constexpr (DT == ZERO_F32) {
+        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+        out[0] = f.x; out[1] = f.y; out[2] = f.z; out[3] = f.w;
+    } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        out[0] = cvt16<DT>(w.x & 0xffffu);
+        out[1] = cvt16<DT>(w.x >> 16);
+        out[2] = cvt16<DT>(w.y & 0xffffu);
+        out[3] = cvt16<DT>(w.y >> 16);
+    }
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ double wave_sum(double x) {
+    // xor butterfly: every lane ends with the same, order-fixed sum
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+// block-wide sum, fixed order; the result is valid in thread 0
+__device__ __forceinline__ double block_sum(double x) {
+    __shared__ double sh[kWaves];
+    x = wave_sum(x);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) t += sh[w];
+    }
+    return t;
+}
+
+// ---------------------------------------------------------------- step scalars
+struct StepScalars {
+    int skip;
+    float coef, inv, bc1, bc2;
+};
+
+// The per-step decisions, read from the device state by every block (and by
+// the finalize kernel): overflow across ranks -> skip; global-norm clip
+// coefficient; exact reciprocal of the power-of-two loss scale; bias
+// corrections with t = step + 1.
+__device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, double beta1,
+                                                 double beta2, double max_norm) {
+    StepScalars s;
+    s.skip = (st->overflow | st->remote_overflow) != 0;
+    const double total = st->sumsq + st->remote_sumsq;
+    s.coef = 1.0f;
+    if (max_norm > 0.0) {
+        const double c = max_norm / (sqrt(total) + 1e-6);
+        s.coef = (float)(c < 1.0 ? c : 1.0);
+    }
+    s.inv = (float)(1.0 / (double)st->loss_scale);
+    s.bc1 = (float)(1.0 - st->beta1_pow * beta1);
+    s.bc2 = (float)(1.0 - st->beta2_pow * beta2);
+    return s;
+}
+
+// ---------------------------------------------------------------- reduce + statistics
+// red[i] = sum over buffers in rank order (fp32), AVG -> / n_ranks; optional
+// statistics of u = red * (1/loss_scale): per-block fp64 partial of u^2 into
+// st->partials[block] and an overflow flag.  A fold kernel adds the partials
+// into st->sumsq in a fixed order, so the sum is reproducible.
+template <int DT, bool VEC, bool WRITE, bool STATS>
+__global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float inv_n,
+                                                          int pow2_n) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int64_t n = a.n;
+    const int N = a.n_ranks;
+    float inv_scale = 1.0f;
+    if constexpr (STATS) inv_scale = (float)(1.0 / (double)a.st->loss_scale);
+    const float fN = (float)N;
+
+    double ss = 0.0;
+    int ovf = 0;
+    const int64_t ntiles = (n + kRTile - 1) / kRTile;
+    const int64_t nfull = VEC ? n / kRTile : 0;
+    for (int64_t t = wave_id; t < ntiles; t += nwaves) {
+        const int64_t i0 = t * kRTile + 8 * lane;
+        float acc[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+        const bool full = t < nfull;
+        if (full) {
+            if constexpr (DT == ZERO_F32) {
+                for (int k = 0; k < N; ++k) {
+                    const float* b = static_cast<const float*>(a.bufs[k]) + i0;
+                    const float4 x0 = reinterpret_cast<const float4*>(b)[0];
+                    const float4 x1 = reinterpret_cast<const float4*>(b)[1];
+                    acc[0] = acc[0] + x0.x; acc[1] = acc[1] + x0.y;
+                    acc[2] = acc[2] + x0.z; acc[3] = acc[3] + x0.w;
+                    acc[4] = acc[4] + x1.x; acc[5] = acc[5] + x1.y;
+                    acc[6] = acc[6] + x1.z; acc[7] = acc[7] + x1.w;
+                }
+            } else {
+                constexpr int KC = 8;  // buffers whose loads are issued together
+                int k = 0;
+                for (; k + KC <= N; k += KC) {
+                    uint4 w[KC];
+#pragma unroll
+                    for (int j = 0; j < KC; ++j)
+                        w[j] = *reinterpret_cast<const uint4*>(
+                            static_cast<const uint16_t*>(a.bufs[k + j]) + i0);
+#pragma unroll
+                    for (int j = 0; j < KC; ++j) {  // rank order per element
+                        acc[0] = acc[0] + cvt16<DT>(w[j].x & 0xffffu);
+                        acc[1] = acc[1] + cvt16<DT>(w[j].x >> 16);
+                        acc[2] = acc[2] + cvt16<DT>(w[j].y & 0xffffu);
+                        acc[3] = acc[3] + cvt16<DT>(w[j].y >> 16);
+                        acc[4] = acc[4] + cvt16<DT>(w[j].z & 0xffffu);
+                        acc[5] = acc[5] + cvt16<DT>(w[j].z >> 16);
+                        acc[6] = acc[6] + cvt16<DT>(w[j].w & 0xffffu);
+                        acc[7] = acc[7] + cvt16<DT>(w[j].w >> 16);
+                    }
+                }
+                for (; k < N; ++k) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(
+                        static_cast<const uint16_t*>(a.bufs[k]) + i0);
+                    acc[0] = acc[0] + cvt16<DT>(w.x & 0xffffu);
+                    acc[1] = acc[1] + cvt16<DT>(w.x >> 16);
+                    acc[2] = acc[2] + cvt16<DT>(w.y & 0xffffu);
+                    acc[3] = acc[3] + cvt16<DT>(w.y >> 16);
+                    acc[4] = acc[4] + cvt16<DT>(w.z & 0xffffu);
+                    acc[5] = acc[5] + cvt16<DT>(w.z >> 16);
+                    acc[6] = acc[6] + cvt16<DT>(w.w & 0xffffu);
+                    acc[7] = acc[7] + cvt16<DT>(w.w >> 16);
+                }
+            }
+        } else {
+            for (int k = 0; k < N; ++k) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    if (i0 + c < n) acc[c] = acc[c] + load_one<DT>(a.bufs[k], i0 + c);
+            }
+        }
+        float red[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            red[c] = a.op != ZERO_AVG ? acc[c] : (pow2_n ? acc[c] * inv_n : acc[c] / fN);
+        if constexpr (WRITE) {
+            if (full) {
+                float4* o = reinterpret_cast<float4*>(a.red_out + i0);
+                o[0] = make_float4(red[0], red[1], red[2], red[3]);
+                o[1] = make_float4(red[4], red[5], red[6], red[7]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    if (i0 + c < n) a.red_out[i0 + c] = red[c];
+            }
+        }
+        if constexpr (STATS) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (full || i0 + c < n) {
+                    const float u = red[c] * inv_scale;
+                    ovf |= !isfinite(u);
+                    ss = ss + (double)u * (double)u;
+                }
+            }
+        }
+    }
+    if constexpr (STATS) {
+        const double bs = block_sum(ss);
+        if (threadIdx.x == 0) {
+            a.st->partials[blockIdx.x] = bs;
+            if (blockIdx.x == 0) a.st->n_partials = (int32_t)gridDim.x;
+        }
+        if (__ballot(ovf) != 0ull && lane == 0) atomicOr(&a.st->overflow, 1);
+    }
+}
+
+// st->sumsq += partials[0..n_partials), fixed order (one block)
+__global__ void __launch_bounds__(kThreads) fold_kernel(zero_step_state_t* st) {
+    const int n = st->n_partials;
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += kThreads) s += st->partials[i];
+    s = block_sum(s);
+    if (threadIdx.x == 0) st->sumsq = st->sumsq + s;
+}
+
+// ---------------------------------------------------------------- INT8 of one slice
+// x[4]: this lane's four written values (zero for elements past the end).
+// One 256-element block per wave slice: amax across the wave, then codes.
+__device__ __forceinline__ uint32_t quant_quad(const float x[4], float* scale_out) {
+    float a = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a = fmaxf(a, fabsf(x[c]));
+    const float amax = wave_max(a);
+    const float scale = amax / 127.0f;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        float r = 0.0f;
+        if (amax != 0.0f) {
+            r = rintf(x[c] / scale);  // ties to even
+            if (isnan(r)) r = 0.0f;
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+        }
+        packed |= ((uint32_t)(int32_t)r & 0xffu) << (8 * c);
+    }
+    *scale_out = scale;
+    return packed;
+}
+
+// ---------------------------------------------------------------- AdamW
+template <int GT, int PT, bool QUANT, bool FULL>
+__device__ __forceinline__ void adam_tile(const AdamLaunch& a, const StepScalars& s,
+                                          int64_t base, int lane) {
+    const int64_t n = a.n;
+    float gv[kU][4], pv[kU][4], mv[kU][4], vv[kU][4];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int64_t i0 = base + 256 * u + 4 * lane;
+        if constexpr (FULL) {
+            load_quad<GT>(a.g, i0, gv[u]);
+            load_quad<ZERO_F32>(a.p, i0, pv[u]);
+            load_quad<ZERO_F32>(a.m, i0, mv[u]);
+            load_quad<ZERO_F32>(a.v, i0, vv[u]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool ok = i0 + c < n;
+                gv[u][c] = ok ? load_one<GT>(a.g, i0 + c) : 0.0f;
+                pv[u][c] = ok ? a.p[i0 + c] : 0.0f;
+                mv[u][c] = ok ? a.m[i0 + c] : 0.0f;
+                vv[u][c] = ok ? a.v[i0 + c] : 0.0f;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int64_t i0 = base + 256 * u + 4 * lane;
+        uint32_t lp16[4];
+        float lpv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float uu = gv[u][c] * s.inv;      // unscale
+            const float g = uu * s.coef;            // clip
+            const float mn = a.b1 * mv[u][c] + a.c1 * g;
+            const float vn = a.b2 * vv[u][c] + a.c2 * (g * g);
+            const float mh = mn / s.bc1;
+            const float vh = vn / s.bc2;
+            const float d = sqrtf(vh) + a.eps;
+            const float pn = pv[u][c] * a.wdf - (a.lr * mh) / d;
+            pv[u][c] = pn;
+            mv[u][c] = mn;
+            vv[u][c] = vn;
+            lp16[c] = round16<PT>(pn);
+            lpv[c] = cvt16<PT>(lp16[c]);            // the value the slot now holds
+        }
+        uint16_t* lp = static_cast<uint16_t*>(a.lp);
+        if constexpr (FULL) {
+            *reinterpret_cast<float4*>(a.p + i0) = make_float4(pv[u][0], pv[u][1], pv[u][2], pv[u][3]);
+            *reinterpret_cast<float4*>(a.m + i0) = make_float4(mv[u][0], mv[u][1], mv[u][2], mv[u][3]);
+            *reinterpret_cast<float4*>(a.v + i0) = make_float4(vv[u][0], vv[u][1], vv[u][2], vv[u][3]);
+            *reinterpret_cast<uint2*>(lp + i0) =
+                make_uint2(lp16[0] | (lp16[1] << 16), lp16[2] | (lp16[3] << 16));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (i0 + c < n) {
+                    a.p[i0 + c] = pv[u][c];
+                    a.m[i0 + c] = mv[u][c];
+                    a.v[i0 + c] = vv[u][c];
+                    lp[i0 + c] = (uint16_t)lp16[c];
+                } else {
+                    lpv[c] = 0.0f;
+                }
+            }
+        }
+        if constexpr (QUANT) {
+            float scale;
+            const uint32_t q = quant_quad(lpv, &scale);  // whole wave takes part
+            if constexpr (FULL) {
+                *reinterpret_cast<uint32_t*>(a.q + i0) = q;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (i0 + c < n) a.q[i0 + c] = (int8_t)((q >> (8 * c)) & 0xffu);
+            }
+            const int64_t blk0 = base + 256 * u;
+            if (lane == 0 && blk0 < n) a.qs[blk0 / 256] = scale;
+        }
+    }
+}
+
+template <int GT, int PT, bool QUANT, bool VEC>
+__global__ void __launch_bounds__(kThreads) adamw_kernel(AdamLaunch a) {
+    const StepScalars s = read_step(a.st, a.beta1, a.beta2, a.max_norm);
+    if (s.skip) return;  // overflow on this or another rank: nothing is written
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int64_t ntiles = (a.n + kTile - 1) / kTile;
+    const int64_t nfull = VEC ? a.n / kTile : 0;
+    for (int64_t t = wave_id; t < ntiles; t += nwaves) {
+        if (t < nfull) adam_tile<GT, PT, QUANT, true>(a, s, t * kTile, lane);
+        else adam_tile<GT, PT, QUANT, false>(a, s, t * kTile, lane);
+    }
+}
+
+// Loss scaler and counters after the step (one thread).
+__global__ void finalize_kernel(zero_step_state_t* st, double beta1, double beta2,
+                                double max_norm) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    const StepScalars s = read_step(st, beta1, beta2, max_norm);
+    st->last_norm = sqrt(st->sumsq + st->remote_sumsq);
+    st->last_skipped = s.skip;
+    st->last_coef = s.skip ? 0.0f : s.coef;
+    if (s.skip) {
+        if (st->dynamic) {
+            const float h = st->loss_scale / 2.0f;
+            st->loss_scale = h > st->min_scale ? h : st->min_scale;
+        }
+        st->good_steps = 0;
+    } else {
+        st->step = st->step + 1;
+        st->beta1_pow = st->beta1_pow * beta1;
+        st->beta2_pow = st->beta2_pow * beta2;
+        if (st->dynamic) {
+            st->good_steps = st->good_steps + 1;
+            if (st->good_steps == st->window) {
+                st->loss_scale = st->loss_scale * 2.0f;
+                st->good_steps = 0;
+            }
+        }
+    }
+    st->sumsq = 0.0;
+    st->overflow = 0;
+}
+
+// ---------------------------------------------------------------- standalone INT8
+template <int DT, bool VEC>
+__global__ void __launch_bounds__(kThreads) quant_kernel(QuantLaunch a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int64_t n = a.n;
+    const int64_t ntiles = (n + kTile - 1) / kTile;
+    const int64_t nfull = VEC ? n / kTile : 0;
+    for (int64_t t = wave_id; t < ntiles; t += nwaves) {
+        const bool full = t < nfull;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i0 = t * kTile + 256 * u + 4 * lane;
+            float x[4];
+            if (full) {
+                load_quad<DT>(a.x, i0, x);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[c] = i0 + c < n ? load_one<DT>(a.x, i0 + c) : 0.0f;
+            }
+            float scale;
+            const uint32_t q = quant_quad(x, &scale);
+            if (full) {
+                *reinterpret_cast<uint32_t*>(a.q + i0) = q;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (i0 + c < n) a.q[i0 + c] = (int8_t)((q >> (8 * c)) & 0xffu);
+            }
+            const int64_t blk0 = t * kTile + 256 * u;
+            if (lane == 0 && blk0 < n) a.qs[blk0 / 256] = scale;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launch helpers
+int grid_for_tiles(int64_t ntiles, int cap) {
+    int64_t g = (ntiles + kWaves - 1) / kWaves;
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+template <int DT, bool VEC, bool WRITE, bool STATS>
+int launch_reduce_t(const ReduceLaunch& a, void* stream) {
+    const int64_t ntiles = (a.n + kRTile - 1) / kRTile;
+    const int grid = grid_for_tiles(ntiles, kMaxGridReduce);
+    const int N = a.n_ranks;
+    const int pow2 = (N & (N - 1)) == 0;
+    const float inv_n = 1.0f / (float)N;  // exact when N is a power of two
+    hipLaunchKernelGGL((reduce_kernel<DT, VEC, WRITE, STATS>), dim3(grid), dim3(kThreads), 0,
+                       (hipStream_t)stream, a, inv_n, pow2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    if (STATS) {
+        hipLaunchKernelGGL(fold_kernel, dim3(1), dim3(kThreads), 0, (hipStream_t)stream, a.st);
+        e = hipGetLastError();
+    }
+    return (int)e;
+}
+
+template <int DT, bool VEC>
+int launch_reduce_d(const ReduceLaunch& a, void* stream) {
+    const bool write = a.red_out != nullptr;
+    const bool stats = a.st != nullptr;
+    if (write && stats) return launch_reduce_t<DT, VEC, true, true>(a, stream);
+    if (write) return launch_reduce_t<DT, VEC, true, false>(a, stream);
+    return launch_reduce_t<DT, VEC, false, true>(a, stream);
+}
+
+template <int DT>
+int launch_reduce_v(const ReduceLaunch& a, void* stream) {
+    return a.vec ? launch_reduce_d<DT, true>(a, stream) : launch_reduce_d<DT, false>(a, stream);
+}
+
+template <int GT, int PT, bool QUANT>
+int launch_adamw_q(const AdamLaunch& a, void* stream) {
+    const int64_t ntiles = (a.n + kTile - 1) / kTile;
+    const int grid = grid_for_tiles(ntiles, kMaxGridStep);
+    if (a.vec)
+        hipLaunchKernelGGL((adamw_kernel<GT, PT, QUANT, true>), dim3(grid), dim3(kThreads), 0,
+                           (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL((adamw_kernel<GT, PT, QUANT, false>), dim3(grid), dim3(kThreads), 0,
+                           (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+template <int GT, int PT>
+int launch_adamw_p(const AdamLaunch& a, void* stream) {
+    return a.q ? launch_adamw_q<GT, PT, true>(a, stream) : launch_adamw_q<GT, PT, false>(a, stream);
+}
+
+template <int GT>
+int launch_adamw_g(const AdamLaunch& a, void* stream) {
+    return a.pdtype == ZERO_F16 ? launch_adamw_p<GT, ZERO_F16>(a, stream)
+                                : launch_adamw_p<GT, ZERO_BF16>(a, stream);
+}
+
+}  // namespace
+
+int launch_reduce_stats(const ReduceLaunch& a, void* stream) {
+    switch (a.dtype) {
+        case ZERO_F32: return launch_reduce_v<ZERO_F32>(a, stream);
+        case ZERO_F16: return launch_reduce_v<ZERO_F16>(a, stream);
+        default: return launch_reduce_v<ZERO_BF16>(a, stream);
+    }
+}
+
+int launch_adamw(const AdamLaunch& a, void* stream) {
+    if (a.n > 0) {
+        int e;
+        switch (a.gdtype) {
+            case ZERO_F32: e = launch_adamw_g<ZERO_F32>(a, stream); break;
+            case ZERO_F16: e = launch_adamw_g<ZERO_F16>(a, stream); break;
+            default: e = launch_adamw_g<ZERO_BF16>(a, stream); break;
+        }
+        if (e != 0) return e;
+    }
+    if (a.flags & ZERO_STEP_FINALIZE) {
+        hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, a.st,
+                           a.beta1, a.beta2, a.max_norm);
+        return (int)hipGetLastError();
+    }
+    return 0;
+}
+
+int launch_quant(const QuantLaunch& a, void* stream) {
+    const int64_t ntiles = (a.n + kTile - 1) / kTile;
+    const int grid = grid_for_tiles(ntiles, kMaxGridStep);
+    if (a.dtype == ZERO_F16) {
+        if (a.vec)
+            hipLaunchKernelGGL((quant_kernel<ZERO_F16, true>), dim3(grid), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+        else
+            hipLaunchKernelGGL((quant_kernel<ZERO_F16, false>), dim3(grid), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+    } else {
+        if (a.vec)
+            hipLaunchKernelGGL((quant_kernel<ZERO_BF16, true>), dim3(grid), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+        else
+            hipLaunchKernelGGL((quant_kernel<ZERO_BF16, false>), dim3(grid), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+    }
+    return (int)hipGetLastError();
+}
+
+const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
+
+}  // namespace zf

@@ -1,0 +1,57 @@
+// zf_launch.h -- internal interface between the C-ABI layer (zeroflat_api.cpp)
+// and the gfx950 kernels (zeroflat_kernels.hip).  Arguments reaching these
+// launchers have been validated; they only pick a kernel variant and launch.
+#pragma once
+
+#include <stdint.h>
+
+#include "zeroflat.h"
+
+namespace zf {
+
+// Reduce (n_ranks buffers) or statistics-only (n_ranks == 1, red_out == null)
+// over [0, n) of each buffer (pointers already offset to the rank's slice).
+struct ReduceLaunch {
+    const void* bufs[ZERO_MAX_RANKS];
+    int32_t n_ranks;
+    int32_t dtype;   // zero_dtype_t of the inputs
+    int32_t op;      // zero_reduce_op_t
+    int32_t vec;     // 1: every pointer allows 16-byte accesses
+    int64_t n;
+    float* red_out;  // may be null
+    zero_step_state_t* st;  // may be null
+};
+int launch_reduce_stats(const ReduceLaunch& a, void* stream);
+
+struct AdamLaunch {
+    const void* g;
+    int32_t gdtype;
+    int32_t pdtype;
+    float* p;
+    float* m;
+    float* v;
+    int64_t n;
+    void* lp;        // All-Gather slot, already offset
+    int8_t* q;       // INT8 slot, already offset (or null)
+    float* qs;       // scales of the slot, already offset
+    int32_t vec;     // 1: vector path allowed
+    uint32_t flags;
+    float b1, c1, b2, c2, lr, wdf, eps;
+    double beta1, beta2, max_norm;
+    zero_step_state_t* st;
+};
+int launch_adamw(const AdamLaunch& a, void* stream);
+
+struct QuantLaunch {
+    const void* x;
+    int32_t dtype;
+    int32_t vec;
+    int64_t n;
+    int8_t* q;
+    float* qs;
+};
+int launch_quant(const QuantLaunch& a, void* stream);
+
+const char* hip_error_string(int err);
+
+}  // namespace zf

@@ -1,0 +1,56 @@
+"""One rank's optimizer over its FlatParameter shard: owns the fp32 master, m,
+v and the device step state, and issues the library calls of one step in the
+order the pages give (reduce or statistics, then the fused AdamW step).  No
+arithmetic happens here; every part of the step runs in libzeroflat.
+"""
+import torch
+
+from . import (ZERO_AVG, StepState, zero_adamw_shard_step, zero_grad_reduce_shard,
+               zero_unscale_norm)
+
+
+class ShardOptimizer:
+    def __init__(self, master, hp, loss_scale=65536.0, dynamic=False, window=1000,
+                 min_scale=1.0, quant_block=0):
+        if master.dtype != torch.float32 or not master.is_cuda or not master.is_contiguous():
+            raise ValueError("master must be a contiguous float32 CUDA tensor")
+        self.master = master
+        self.exp_avg = torch.zeros_like(master)
+        self.exp_avg_sq = torch.zeros_like(master)
+        self.hp = dict(hp)
+        self.state = StepState(loss_scale, dynamic, window, min_scale, device=master.device)
+        self.quant_block = quant_block
+        self._red = None
+
+    @property
+    def numel(self):
+        return self.master.numel()
+
+    def reduced_buffer(self):
+        if self._red is None:
+            self._red = torch.empty_like(self.master)
+        return self._red
+
+    def step_from_rank_buffers(self, grad_bufs, elem_offset, allgather_buf, slot_offset,
+                               op=ZERO_AVG, q_buf=None, q_scales=None, q_slot_offset=0,
+                               q_scale_offset=0, stream=None):
+        """Reduce-Scatter's reduce over the N rank buffers, then the step."""
+        red = self.reduced_buffer()
+        zero_grad_reduce_shard(grad_bufs, elem_offset, self.numel, op, red, self.state,
+                               stream=stream)
+        self._apply(red, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
+                    q_scale_offset, stream)
+
+    def step_from_reduced(self, grad_shard, allgather_buf, slot_offset, q_buf=None,
+                          q_scales=None, q_slot_offset=0, q_scale_offset=0, stream=None):
+        """Statistics over an already reduced (fp32/fp16/bf16) shard, then the step."""
+        zero_unscale_norm(grad_shard, self.state, n=self.numel, stream=stream)
+        self._apply(grad_shard, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
+                    q_scale_offset, stream)
+
+    def _apply(self, grad, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
+               q_scale_offset, stream):
+        zero_adamw_shard_step(grad, self.master, self.exp_avg, self.exp_avg_sq, allgather_buf,
+                              slot_offset, self.hp, self.state, q_buf=q_buf, q_scales=q_scales,
+                              q_slot_offset=q_slot_offset, q_scale_offset=q_scale_offset,
+                              q_block=self.quant_block or 256, finalize=True, stream=stream)

@@ -1,0 +1,258 @@
+/*
+ * zeroflat.h -- C ABI of libzeroflat: one rank's sharded mixed-precision
+ * AdamW step over a FlatParameter, on one AMD Instinct MI355X (gfx950).
+ *
+ * The step, as the pages describe it, and the call that performs each part:
+ *   1. zero_flat_layout        FlatParameter offsets, equal padded shards and
+ *                              per-rank memory accounting (host only).
+ *   2. zero_grad_reduce_shard  reduce half of Reduce-Scatter: sum or average
+ *                              N ranks' fp16/bf16 gradient buffers over this
+ *                              rank's slice, fused with the overflow test and
+ *                              the sum of squares of the unscaled gradient.
+ *      zero_unscale_norm       the same statistics over an already reduced
+ *                              (or pre-reduced fp16/bf16) gradient shard.
+ *   3. zero_adamw_shard_step   skip-on-overflow, global-norm clipping, fused
+ *                              AdamW on the fp32 master/m/v shard, fp16/bf16
+ *                              write-back into the rank's All-Gather slot,
+ *                              optional blockwise INT8 of that slot, and the
+ *                              loss-scaler / step-counter update.
+ *   4. zero_quant_allgather_slot  blockwise INT8 of an existing slot.
+ *
+ * Sources (three web pages, cited by title and section):
+ *   "DeepSpeed 与 FSDP" (docs.ifdog.com): ZeRO-1/2/3 memory arithmetic,
+ *       ZeRO-2 Reduce-Scatter, ZeRO-Offload Adam equations, FlatParameter,
+ *       ZeRO++ quantised All-Gather, the numpy 4-rank simulation.
+ *   "PyTorch FSDP（Fully Sharded Data Parallel）源码级深度解析" (tbr8.org):
+ *       §3.1 FlatParameter _param_infos, §3.3 reduce_scatter_tensor(AVG|SUM),
+ *       §7.2 fp32 master weights under MixedPrecision.
+ *   ZeRO paper reading at 2kiu.com/news/5312103: §5.1 DeepSpeed config (AdamW
+ *       hyper-parameters, fp16 dynamic loss scale, gradient clipping),
+ *       §5.2 ZeRO == DDP, §5.3 overflow/clipping must agree across ranks.
+ *
+ * Conventions shared by every entry point:
+ *   - Return ZERO_OK (0) or a negative zero_status_t; nothing throws.  After a
+ *     failure zero_last_error() returns a thread-local message.  Arguments are
+ *     validated before anything is launched: on error nothing ran.
+ *   - Device pointers are owned by the caller; the library never allocates
+ *     or frees memory and never synchronizes.  It cannot see allocation
+ *     sizes: the caller vouches that every range it names is allocated.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); all
+ *     kernels of a call are enqueued on it, in order.
+ *   - Element counts and offsets are int64 (slot offsets exceed 2^31).
+ *   - One zero_step_state_t must not be used by two streams at once.
+ */
+#ifndef ZEROFLAT_H
+#define ZEROFLAT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ZERO_OK = 0,
+    ZERO_EINVAL = -1, /* bad argument (null pointer, bad enum, negative size ...) */
+    ZERO_EALIGN = -2, /* a pointer is not aligned to its element size */
+    ZERO_ERANGE = -3, /* a size or count exceeds what the library supports */
+    ZERO_EHIP = -4    /* a HIP launch failed; zero_last_error() has HIP's text */
+} zero_status_t;
+
+typedef enum { ZERO_F32 = 0, ZERO_F16 = 1, ZERO_BF16 = 2 } zero_dtype_t;
+typedef enum { ZERO_SUM = 0, ZERO_AVG = 1 } zero_reduce_op_t;
+
+#define ZERO_MAX_RANKS 256      /* gradient buffers one reduce call can read */
+#define ZERO_MAX_PARTIALS 2048  /* per-block partial sums kept in the state */
+
+/* Message for the last failure on this thread ("" if none). */
+const char* zero_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * 1. FlatParameter layout and memory accounting (host only, integer).
+ *
+ * "PyTorch FSDP 源码级深度解析" §3.1: the parameters are concatenated in
+ * order into one 1-D FlatParameter, parameter j occupying [start_j, end_j)
+ * with no gap.  "DeepSpeed 与 FSDP", FlatParameter section: every rank holds
+ * 1/N of it.  Shard rule (the pages give three that disagree on remainders):
+ * S = ceil(T/N) rounded up to a multiple of `align`, padded = N*S, the
+ * padded - T tail elements are zero padding; rank r owns [r*S, (r+1)*S).
+ * Accounting ("DeepSpeed 与 FSDP", 逐步推导 and ZeRO-3 的数学总结) with
+ * param_bytes P, grad_bytes G, optimizer bytes K per parameter (2, 2, 12 for
+ * fp16 params/grads + fp32 master/m/v; 2, 2, 8 when the optimizer keeps only
+ * m and v), per rank: DP (P+G+K)*T; ZeRO-1 (P+G)*T + K*S;
+ * ZeRO-2 P*T + (G+K)*S; ZeRO-3 (P+G+K)*S.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int64_t start, end; /* flat [start, end) of one parameter */
+} zero_span_t;
+
+typedef struct {
+    int32_t param;        /* parameter index, or -1 for the zero padding */
+    int32_t reserved;
+    int64_t off_in_param; /* first element within the parameter (or padding) */
+    int64_t off_in_shard; /* where the piece starts within the rank's shard */
+    int64_t len;          /* elements */
+} zero_segment_t;
+
+typedef struct {
+    int64_t total;   /* T = sum of numels */
+    int64_t shard;   /* S */
+    int64_t padded;  /* N * S */
+    int64_t pad;     /* padded - T */
+    int32_t n_ranks;
+    int32_t reserved;
+    int64_t align;
+    int64_t bytes_dp, bytes_z1, bytes_z2, bytes_z3; /* per rank */
+} zero_layout_t;
+
+/* numels[n_params] (each >= 0), 1 <= n_ranks, align >= 1, 0 <= rank < n_ranks.
+ * Writes *out; spans[n_params] if spans != NULL; the pieces of rank `rank`'s
+ * shard in flat order (parameters first, then padding) to segs[0..segs_cap)
+ * if segs != NULL, and their count to *n_segs if n_segs != NULL.  Returns
+ * ZERO_ERANGE (with *n_segs = the count needed) if segs_cap is too small or
+ * a product overflows int64. */
+int zero_flat_layout(const int64_t* numels, int32_t n_params, int32_t n_ranks, int64_t align,
+                     int32_t param_bytes, int32_t grad_bytes, int32_t optim_bytes,
+                     int32_t rank, zero_layout_t* out, zero_span_t* spans,
+                     zero_segment_t* segs, int32_t segs_cap, int32_t* n_segs);
+
+/* ------------------------------------------------------------------------
+ * Step state.  Device-resident, caller-allocated (sizeof(zero_step_state_t)
+ * bytes, 8-byte aligned), initialised from a host copy filled by
+ * zero_step_state_init.  The library reads and updates it on the stream, so
+ * the skip and loss-scale decisions never leave the device.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    /* accumulated over the current step by the reduce / unscale_norm calls */
+    double sumsq;            /* local sum of squares of the unscaled gradient */
+    int32_t overflow;        /* 1 if any local unscaled gradient is inf/NaN */
+    /* other ranks' contributions: the one-GPU stand-in for the cross-rank
+     * all-reduce of (sumsq, overflow) ("2kiu.com §5.3": overflow and
+     * clipping must agree on every rank).  Set by the caller, never reset. */
+    int32_t remote_overflow;
+    double remote_sumsq;
+    /* loss scaler (2kiu.com §5.1: "loss_scale": 0 = dynamic,
+     * initial_scale_power 16, loss_scale_window 1000) */
+    float loss_scale;        /* current scale, a power of two */
+    float min_scale;         /* floor when halving */
+    int32_t dynamic;         /* 0 = static scale */
+    int32_t window;          /* good steps before the scale doubles */
+    int32_t good_steps;      /* consecutive steps without overflow */
+    int32_t step;            /* successful (applied) steps so far; t = step + 1 */
+    double beta1_pow;        /* beta1^step, by successive double products */
+    double beta2_pow;        /* beta2^step */
+    /* results of the last finished step */
+    double last_norm;        /* sqrt(sumsq + remote_sumsq) */
+    float last_coef;         /* clip coefficient applied */
+    int32_t last_skipped;    /* 1 if the step was skipped (overflow) */
+    /* internal: per-block partial sums of the last statistics launch */
+    int32_t n_partials;
+    int32_t reserved;
+    double partials[ZERO_MAX_PARTIALS];
+} zero_step_state_t;
+
+/* Fill a HOST zero_step_state_t for step 0: loss_scale must be a power of
+ * two >= min_scale >= 1 (the unscale is then exact); dynamic != 0 needs
+ * window >= 1.  The caller copies it to device memory. */
+int zero_step_state_init(zero_step_state_t* host_state, float loss_scale, int32_t dynamic,
+                         int32_t window, float min_scale);
+
+/* ------------------------------------------------------------------------
+ * 2. Reduce half of Reduce-Scatter, with fused step statistics.
+ *
+ * "DeepSpeed 与 FSDP", ZeRO-2 and the numpy simulation: every rank's
+ * gradients are summed and this rank keeps its slice; "PyTorch FSDP
+ * 源码级深度解析" §3.3: the op is AVG or SUM; "DeepSpeed 与 FSDP", 实践要点:
+ * the reduction runs in fp32.  For i in [0, shard_numel):
+ *     acc = 0; for k = 0..n_ranks-1 (rank order): acc += f32(grad_bufs[k][elem_offset + i])
+ *     red_out[i] = (op == ZERO_AVG) ? acc / n_ranks : acc          (fp32, IEEE)
+ * grad_bufs: HOST array of n_ranks DEVICE pointers, each fp16 or bf16
+ *   (in_dtype), each valid over [elem_offset, elem_offset + shard_numel) --
+ *   full padded flat buffers with elem_offset = r*S, or per-rank slices with
+ *   elem_offset = 0.  1 <= n_ranks <= ZERO_MAX_RANKS.
+ * red_out: DEVICE fp32[shard_numel], must not alias the inputs.
+ * d_state: DEVICE state or NULL.  If set, with u_i = red_out[i] * (1/loss_scale):
+ *   sumsq += sum_i (double)u_i^2 (deterministic order for a given size),
+ *   overflow |= any(!isfinite(u_i)).
+ * ---------------------------------------------------------------------- */
+int zero_grad_reduce_shard(const void* const* grad_bufs, int32_t n_ranks, int32_t in_dtype,
+                           int64_t elem_offset, int64_t shard_numel, int32_t op,
+                           float* red_out, zero_step_state_t* d_state, void* stream);
+
+/* Statistics only, over an already reduced fp32 shard or a pre-reduced
+ * fp16/bf16 gradient shard (DEVICE grad_shard[n] of `dtype`): the sumsq /
+ * overflow accumulation described above, u_i = f32(grad_shard[i]) / loss_scale. */
+int zero_unscale_norm(const void* grad_shard, int32_t dtype, int64_t n,
+                      zero_step_state_t* d_state, void* stream);
+
+/* ------------------------------------------------------------------------
+ * 3. Fused AdamW shard step.
+ *
+ * "DeepSpeed 与 FSDP", ZeRO-Offload: Adam with bias correction,
+ *   m_t = b1 m + (1-b1) g,  v_t = b2 v + (1-b2) g^2,
+ *   mh = m_t/(1-b1^t),  vh = v_t/(1-b2^t),  p -= lr * mh/(sqrt(vh)+eps);
+ * 2kiu.com §5.1: AdamW (decoupled decay: p_{t-1} scaled by 1 - lr*wd) and
+ * gradient_clipping; "PyTorch FSDP 源码级深度解析" §7.2: the update runs on
+ * the fp32 master and the fp16/bf16 copy is what the All-Gather sends.
+ *
+ * Order, all on the device, per call:
+ *   total = sumsq + remote_sumsq; ovf = overflow | remote_overflow
+ *   if ovf: nothing below is written (skip-step)
+ *   else:   coef = (float) min(1, max_grad_norm / (sqrt(total) + 1e-6))
+ *           (1 if max_grad_norm <= 0), t = step + 1, and per element, each
+ *           a separately rounded fp32 operation:
+ *             u = f32(grad[i]) * (1/loss_scale);  g = u * coef
+ *             m = b1*m + c1*g;  v = b2*v + c2*(g*g)
+ *             mh = m / bc1;  vh = v / bc2;  d = sqrtf(vh) + eps
+ *             p = p*wdf - (lr*mh) / d
+ *             allgather_buf[slot_offset + i] = round_nearest_even(p)  (param_dtype)
+ *           with b1 = f32(beta1), c1 = f32(1-beta1), b2, c2 likewise,
+ *           bc1 = f32(1 - beta1^t), bc2 = f32(1 - beta2^t),
+ *           lr = f32(lr), wdf = f32(1 - lr*wd), eps = f32(eps).
+ *   if q_buf != NULL (ZeRO++ quantised All-Gather payload, "DeepSpeed 与
+ *   FSDP", ZeRO++; 2kiu.com §4.2): per block b of q_block written values
+ *   (blocks start at the shard start; the last may be short):
+ *     scale_b = amax_b / 127.0f;  q = amax_b == 0 ? 0 : clamp(rint(x/scale_b), -127, 127)
+ *     q_buf[q_slot_offset + i] = q;  q_scales[q_scale_offset + b] = scale_b
+ *   if (flags & ZERO_STEP_FINALIZE): loss scaler and counters -- on overflow
+ *     scale = max(scale/2, min_scale) if dynamic, good_steps = 0; else
+ *     step += 1, beta pows *= betas, and if dynamic good_steps += 1 with the
+ *     scale doubled (good_steps = 0) when good_steps reaches window; then
+ *     sumsq = 0 and overflow = 0 for the next step, last_* filled in.
+ *     Pass it on the last (or only) FlatParameter of the optimizer step.
+ *
+ * grad_shard: DEVICE grad_dtype[n] -- the fp32 output of zero_grad_reduce_shard
+ *   or a pre-reduced fp16/bf16 shard.
+ * master, exp_avg, exp_avg_sq: DEVICE fp32[n], updated in place.
+ * allgather_buf: DEVICE param_dtype (fp16/bf16) buffer valid over
+ *   [slot_offset, slot_offset + n).
+ * q_buf/q_scales: NULL, or DEVICE int8 and fp32 buffers valid over
+ *   [q_slot_offset, +n) and [q_scale_offset, +ceil(n/q_block)); q_block == 256.
+ * hp: HOST hyper-parameters; betas must stay fixed for the life of d_state.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    double max_grad_norm; /* <= 0: no clipping */
+} zero_adamw_hparams_t;
+
+#define ZERO_STEP_FINALIZE 1u
+
+int zero_adamw_shard_step(const void* grad_shard, int32_t grad_dtype, float* master,
+                          float* exp_avg, float* exp_avg_sq, int64_t n, void* allgather_buf,
+                          int32_t param_dtype, int64_t slot_offset, int8_t* q_buf,
+                          float* q_scales, int64_t q_slot_offset, int64_t q_scale_offset,
+                          int32_t q_block, const zero_adamw_hparams_t* hp, uint32_t flags,
+                          zero_step_state_t* d_state, void* stream);
+
+/* ------------------------------------------------------------------------
+ * 4. Blockwise INT8 of an existing fp16/bf16 slot (DEVICE slot[n]), the
+ * same definition as the fused epilogue above; block == 256.
+ * ---------------------------------------------------------------------- */
+int zero_quant_allgather_slot(const void* slot, int32_t dtype, int64_t n, int32_t block,
+                              int8_t* q_buf, int64_t q_slot_offset, float* q_scales,
+                              int64_t q_scale_offset, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -11,7 +11,7 @@
  *   z ^= z>>31.  Element j sums the twelve 16-bit fields of outputs 3j..3j+2
  *   (Irwin-Hall(12)): z = (2*sum - 786420) * 2^-17, exact in integers and
  *   exactly representable in binary32; value = z * sigma (one rounding),
- *   then rounded to nearest-even into the storage format.
+ *   then rounded to nearest-even into the storage format (on the bits).
  */
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,13 +38,34 @@ __device__ __forceinline__ float unit_variate(uint64_t key, uint64_t j) {
     return (float)zi * 0x1p-17f;
 }
 
-template <typename T>
+/* Round-to-nearest-even of binary32 to the storage format, on the bit
+ * patterns (no hardware conversion mode involved). */
+__device__ __forceinline__ uint16_t to_half_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    const uint32_t a = u & 0x7fffffffu;
+    uint32_t h;
+    if (a >= 0x7f800000u) h = a > 0x7f800000u ? 0x7e00u : 0x7c00u;
+    else if (a >= 0x477ff000u) h = 0x7c00u;
+    else if (a >= 0x38800000u) { const uint32_t m = a - 0x38000000u; h = (m + 0xfffu + ((m >> 13) & 1u)) >> 13; }
+    else h = __float_as_uint(__uint_as_float(a) + 0.5f) - 0x3f000000u;
+    return (uint16_t)(sign | h);
+}
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int DT, typename T>
 __global__ void __launch_bounds__(256) fill_normal(uint64_t key, int64_t start, int64_t n,
                                                    float sigma, T* __restrict__ out) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         const float x = unit_variate(key, (uint64_t)(start + i)) * sigma;
-        out[i] = static_cast<T>(x); /* round to nearest even */
+        if constexpr (DT == 0) out[i] = x;
+        else if constexpr (DT == 1) out[i] = to_half_bits(x);
+        else out[i] = to_bf16_bits(x);
     }
 }
 
@@ -76,14 +97,14 @@ int synth_fill_normal(uint64_t key, int64_t start, int64_t n, float sigma, void*
     hipStream_t s = (hipStream_t)stream;
     const int g = grid_for(n);
     if (dtype == 0)
-        hipLaunchKernelGGL(fill_normal<float>, dim3(g), dim3(256), 0, s, key, start, n, sigma,
-                           (float*)out);
+        hipLaunchKernelGGL((fill_normal<0, float>), dim3(g), dim3(256), 0, s, key, start, n,
+                           sigma, (float*)out);
     else if (dtype == 1)
-        hipLaunchKernelGGL(fill_normal<_Float16>, dim3(g), dim3(256), 0, s, key, start, n,
-                           sigma, (_Float16*)out);
+        hipLaunchKernelGGL((fill_normal<1, uint16_t>), dim3(g), dim3(256), 0, s, key, start, n,
+                           sigma, (uint16_t*)out);
     else if (dtype == 2)
-        hipLaunchKernelGGL(fill_normal<__bf16>, dim3(g), dim3(256), 0, s, key, start, n, sigma,
-                           (__bf16*)out);
+        hipLaunchKernelGGL((fill_normal<2, uint16_t>), dim3(g), dim3(256), 0, s, key, start, n,
+                           sigma, (uint16_t*)out);
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();

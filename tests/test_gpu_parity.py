@@ -1,0 +1,414 @@
+"""GPU parity: libzeroflat (through its C ABI) against the CPU oracle on the
+same seeded inputs, at sizes that span several tiles and a ragged tail, on
+the vector and the element-wise paths, plus the edge cases of the step.
+
+Bar: bit-exact for layout, flags, INT8 codes and (by construction of the
+fp32 operation order) master/m/v and the 16-bit slot; the global norm within
+1e-5 relative (reduction order differs)."""
+import numpy as np
+import pytest
+import torch
+
+from harness import OracleRank, assert_bitwise, to_dev, to_host
+from oracle import oracle as orc
+from synth import synth
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=3e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=1.0)
+
+
+@pytest.fixture(scope="module")
+def zf():
+    import fsdp_sharded_mixed_flatparameter_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rel(a, b):
+    return abs(a - b) / max(abs(b), 1e-300)
+
+
+# ------------------------------------------------------------------ generator
+@pytest.mark.parametrize("code", [0, 1, 2])
+def test_generator_gpu_matches_cpu(zf, code):
+    for start, n in ((0, 1), (0, 1_000_003), (8_750_000_000, 70_001), (2 ** 40 + 5, 513)):
+        say("generator", code, start, n)
+        key = synth.stream_key("gen-test", code, start)
+        t = torch.empty(n, dtype={0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[code],
+                        device="cuda")
+        synth.fill_normal(t, key, start, 0.02)
+        ref = synth.normal(key, start, n, 0.02, code)
+        assert_bitwise(to_host(t), ref, "generator")
+
+
+# ------------------------------------------------------------------ reduce
+REDUCE_CASES = [
+    # (dtype, n_ranks, op, shard, elem_offset)
+    (1, 4, 1, 1, 0), (1, 4, 1, 7, 0), (1, 4, 0, 511, 0), (1, 4, 1, 512, 0),
+    (1, 4, 1, 513, 0), (1, 8, 1, 4096 + 13, 8), (1, 64, 1, 20_000, 0), (1, 3, 1, 1000, 0),
+    (1, 3, 0, 1000, 3), (2, 8, 0, 100_000, 16), (2, 8, 1, 100_000, 16), (2, 8, 1, 9_999, 5),
+    (2, 5, 1, 777, 0), (0, 4, 1, 3000, 4), (0, 2, 0, 3001, 1), (1, 1, 1, 2049, 0),
+    (1, 11, 1, 4097, 0), (2, 17, 0, 5000, 8),
+]
+
+
+@pytest.mark.parametrize("dt,n_ranks,op,shard,off", REDUCE_CASES)
+def test_reduce_shard_parity(zf, dt, n_ranks, op, shard, off):
+    say("reduce", dt, n_ranks, op, shard, off)
+    total = off + shard + 5
+    bufs_h = [synth.normal(synth.stream_key("red", dt, k, shard), 0, total, 1e-3 * (k + 1), dt)
+              for k in range(n_ranks)]
+    bufs_d = [to_dev(b, dt) for b in bufs_h]
+    red_d = torch.full((shard,), float("nan"), device="cuda")
+    state = zf.StepState(65536.0, False)
+    zf.zero_grad_reduce_shard(bufs_d, off, shard, op, red_d, state)
+    red = orc.reduce(bufs_h, dt, off, shard, op)
+    assert_bitwise(to_host(red_d), red, "reduced shard")
+    s_ref, o_ref = orc.unscale_stats(red, orc.F32, 65536.0)
+    st = state.read()
+    assert st.overflow == o_ref == 0
+    assert rel(st.sumsq, s_ref) <= 1e-12
+
+
+def test_reduce_without_state_and_accumulation(zf):
+    """Two reduce calls into one state add their sums of squares."""
+    dt, n = 1, 10_000
+    a = [synth.normal(synth.stream_key("acc", k), 0, n, 1e-3, dt) for k in range(4)]
+    b = [synth.normal(synth.stream_key("acc2", k), 0, n, 1e-3, dt) for k in range(4)]
+    out = torch.empty(n, device="cuda")
+    zf.zero_grad_reduce_shard([to_dev(x, dt) for x in a], 0, n, zf.ZERO_AVG, out, None)
+    assert_bitwise(to_host(out), orc.reduce(a, dt, 0, n, orc.AVG), "no-state reduce")
+    state = zf.StepState(1024.0, True)
+    zf.zero_grad_reduce_shard([to_dev(x, dt) for x in a], 0, n, zf.ZERO_AVG, out, state)
+    zf.zero_grad_reduce_shard([to_dev(x, dt) for x in b], 0, n, zf.ZERO_AVG, out, state)
+    s1, _ = orc.unscale_stats(orc.reduce(a, dt, 0, n, orc.AVG), orc.F32, 1024.0)
+    s2, _ = orc.unscale_stats(orc.reduce(b, dt, 0, n, orc.AVG), orc.F32, 1024.0)
+    assert rel(state.read().sumsq, s1 + s2) <= 1e-12
+
+
+@pytest.mark.parametrize("val", [np.inf, -np.inf, np.nan])
+def test_reduce_overflow_flag(zf, val):
+    dt, n, N = 1, 5000, 4
+    bufs = [synth.normal(synth.stream_key("ovf", k), 0, 2 * n, 1e-3, dt) for k in range(N)]
+    bad = [b.copy() for b in bufs]
+    bad[2][n + 1234] = np.array([val], np.float32).astype(np.float16).view(np.uint16)[0]
+    for bb, expect in ((bufs, 0), (bad, 1)):
+        state = zf.StepState(65536.0, True)
+        out = torch.empty(n, device="cuda")
+        zf.zero_grad_reduce_shard([to_dev(x, dt) for x in bb], n, n, zf.ZERO_AVG, out, state)
+        assert state.read().overflow == expect
+    # an inf outside the rank's slice is not this rank's overflow
+    out_of_slice = [b.copy() for b in bufs]
+    out_of_slice[1][17] = np.float16(np.inf).view(np.uint16)
+    state = zf.StepState(65536.0, True)
+    out = torch.empty(n, device="cuda")
+    zf.zero_grad_reduce_shard([to_dev(x, dt) for x in out_of_slice], n, n, zf.ZERO_AVG, out,
+                              state)
+    assert state.read().overflow == 0
+
+
+@pytest.mark.parametrize("dt,n", [(0, 1), (1, 513), (2, 100_001), (0, 65_536), (1, 3)])
+def test_unscale_norm_parity(zf, dt, n):
+    say("unscale_norm", dt, n)
+    g = synth.normal(synth.stream_key("un", dt, n), 0, n, 1e-3, dt)
+    state = zf.StepState(256.0, False)
+    zf.zero_unscale_norm(to_dev(g, dt), state)
+    s, o = orc.unscale_stats(g, dt, 256.0)
+    st = state.read()
+    assert st.overflow == o and rel(st.sumsq, s) <= 1e-12
+
+
+# ------------------------------------------------------------------ AdamW
+ADAM_CASES = [
+    # (grad dtype, param dtype, n, slot offset, INT8, max_norm, loss scale)
+    (1, 1, 262_528, 0, False, 1.0, 65536.0),
+    (0, 1, 100_000, 100_000, False, 1.0, 65536.0),
+    (2, 2, 4096 * 3 + 100, 8, True, 1.0, 1.0),
+    (2, 2, 1000, 4, True, 1e-4, 1.0),          # clipping active
+    (0, 2, 777, 3, True, 1.0, 2.0 ** 10),      # misaligned slot: element-wise path
+    (1, 1, 511, 1, False, 0.0, 65536.0),       # no clipping, misaligned
+    (1, 2, 1, 0, True, 1.0, 65536.0),
+    (0, 1, 512, 512, True, 1e-3, 1.0),
+    (2, 1, 65_536 + 255, 0, True, 0.5, 1.0),
+]
+
+
+@pytest.mark.parametrize("gdt,pdt,n,slot,quant,max_norm,scale", ADAM_CASES)
+def test_adamw_step_parity(zf, gdt, pdt, n, slot, quant, max_norm, scale):
+    say("adamw", gdt, pdt, n, slot, quant, max_norm, scale)
+    hp = dict(HP, max_grad_norm=max_norm)
+    master0 = synth.normal_f32(synth.stream_key("m0", n), 0, n, 0.02)
+    dev_p = to_dev(master0, 0)
+    dev_m = torch.zeros(n, device="cuda")
+    dev_v = torch.zeros(n, device="cuda")
+    ag = torch.zeros(slot + n + 64, dtype=torch.float16 if pdt == 1 else torch.bfloat16,
+                     device="cuda")
+    nb = -(-n // 256)
+    qb = torch.zeros(slot + n + 64, dtype=torch.int8, device="cuda") if quant else None
+    qs = torch.zeros(nb + 3, device="cuda") if quant else None
+    state = zf.StepState(scale, False)
+    ref = OracleRank(master0, scale, False)
+    for step in range(3):
+        g = synth.normal(synth.stream_key("g", n, step), 0, n, 1e-3 * scale, gdt)
+        dg = to_dev(g, gdt)
+        zf.zero_unscale_norm(dg, state)
+        zf.zero_adamw_shard_step(dg, dev_p, dev_m, dev_v, ag, slot, hp, state,
+                                 q_buf=qb, q_scales=qs, q_slot_offset=slot, q_scale_offset=2)
+        res = ref.step(g, gdt, hp, pdt, quant_block=256 if quant else None)
+        st = state.read()
+        assert st.last_skipped == 0 and st.step == step + 1
+        assert st.last_coef == res["coef"]
+        assert rel(st.last_norm, res["norm"]) <= 1e-5
+        assert_bitwise(to_host(dev_p), ref.p, "master step %d" % step)
+        assert_bitwise(to_host(dev_m), ref.m, "exp_avg step %d" % step)
+        assert_bitwise(to_host(dev_v), ref.v, "exp_avg_sq step %d" % step)
+        lp = to_host(ag)
+        assert_bitwise(lp[slot:slot + n], res["lp"], "slot step %d" % step)
+        assert not lp[:slot].any() and not lp[slot + n:].any(), "wrote outside the slot"
+        if quant:
+            q = to_host(qb)
+            assert_bitwise(q[slot:slot + n].view(np.uint8), res["q"].view(np.uint8), "int8")
+            assert not q[:slot].any() and not q[slot + n:].any()
+            s = to_host(qs)
+            assert_bitwise(s[2:2 + nb], res["scales"], "int8 scales")
+            assert not s[:2].any() and not s[2 + nb:].any()
+
+
+@pytest.mark.parametrize("pdt,n,off", [(1, 4096 + 77, 0), (2, 300_000, 256), (2, 1000, 3),
+                                       (1, 1, 0), (2, 255, 0)])
+def test_quant_slot_parity(zf, pdt, n, off):
+    x = synth.normal(synth.stream_key("q", n), 0, off + n, 0.02, pdt)
+    q = torch.zeros(off + n + 16, dtype=torch.int8, device="cuda")
+    nb = -(-n // 256)
+    s = torch.zeros(nb + 1, device="cuda")
+    zf.zero_quant_allgather_slot(to_dev(x[off:], pdt), q, s, q_slot_offset=off, q_scale_offset=1)
+    rq, rs = orc.quant_int8(np.ascontiguousarray(x[off:]), pdt, 256)
+    qh = to_host(q)
+    assert_bitwise(qh[off:off + n].view(np.uint8), rq.view(np.uint8), "codes")
+    assert not qh[:off].any() and not qh[off + n:].any()
+    assert_bitwise(to_host(s)[1:1 + nb], rs, "scales")
+
+
+def test_quant_special_blocks(zf):
+    """All-zero block, constant block, inf in a block."""
+    x = np.zeros(1024, np.float32)
+    x[256:512] = -0.375
+    x[512:768] = synth.normal_f32(synth.stream_key("sp"), 0, 256, 0.02)
+    x[700] = np.inf
+    x[768:] = synth.normal_f32(synth.stream_key("sp2"), 0, 256, 1e-30)  # bf16 subnormals
+    xb = orc.from_f32(x, orc.BF16)
+    q = torch.zeros(1024, dtype=torch.int8, device="cuda")
+    s = torch.zeros(4, device="cuda")
+    zf.zero_quant_allgather_slot(to_dev(xb, 2), q, s)
+    rq, rs = orc.quant_int8(xb, orc.BF16, 256)
+    assert_bitwise(to_host(q).view(np.uint8), rq.view(np.uint8), "codes")
+    assert_bitwise(to_host(s), rs, "scales")
+
+
+def test_clip_coefficient_matches_oracle(zf):
+    """The fp64 clip coefficient for many global sums of squares, including
+    a remote contribution, computed by the finalize stage of an empty step."""
+    rng = np.random.default_rng(31)
+    vals = list(np.exp(rng.uniform(np.log(1e-12), np.log(1e6), 300))) + [0.0, 1.0, 0.999998]
+    dummy = torch.zeros(1, device="cuda")
+    ag = torch.zeros(1, dtype=torch.float16, device="cuda")
+    for max_norm in (1.0, 0.37, 1e3):
+        for s in vals:
+            state = zf.StepState(1.0, False)
+            host = state.read()
+            host.sumsq = s * 0.75
+            host.remote_sumsq = s * 0.25
+            state.upload(host)
+            zf.zero_adamw_shard_step(dummy[:0], dummy[:0], dummy[:0], dummy[:0], ag, 0,
+                                     dict(HP, max_grad_norm=max_norm), state)
+            st = state.read()
+            ref = orc.clip_coef(s * 0.75 + s * 0.25, max_norm)
+            assert st.last_coef == ref, (s, max_norm, st.last_coef, ref)
+            assert st.last_norm == np.sqrt(s * 0.75 + s * 0.25)
+            assert st.sumsq == 0.0 and st.step == 1
+
+
+def test_skip_step_and_scaler_on_device(zf):
+    """An overflow (local or remote) skips the step: master/m/v, slot and INT8
+    stay bitwise, the scale halves, the step counter holds; a window of good
+    steps doubles the scale."""
+    n, gdt = 3000, 1
+    master0 = synth.normal_f32(synth.stream_key("sk"), 0, n, 0.02)
+    p, m, v = to_dev(master0, 0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    ag = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    qb = torch.zeros(n, dtype=torch.int8, device="cuda")
+    qs = torch.zeros(-(-n // 256), device="cuda")
+    state = zf.StepState(2.0 ** 16, True, window=2)
+    ref = OracleRank(master0, 2.0 ** 16, True, window=2)
+    script = [0, 0, 1, 0, 2, 0, 0, 0]   # 1 = local inf, 2 = remote overflow
+    for step, kind in enumerate(script):
+        g = synth.normal(synth.stream_key("skg", step), 0, n, 1e-3 * 65536, gdt)
+        if kind == 1:
+            g[n // 2] = np.float16(np.inf).view(np.uint16)
+        state.set_remote(0.0, 1 if kind == 2 else 0)
+        before = [to_host(t).copy() for t in (p, m, v, ag, qb, qs)]
+        dg = to_dev(g, gdt)
+        zf.zero_unscale_norm(dg, state)
+        zf.zero_adamw_shard_step(dg, p, m, v, ag, 0, HP, state, q_buf=qb, q_scales=qs)
+        res = ref.step(g, gdt, HP, orc.BF16, remote_overflow=1 if kind == 2 else 0,
+                       quant_block=256)
+        st = state.read()
+        assert st.last_skipped == res["skipped"] == (kind != 0)
+        assert (st.loss_scale, st.good_steps, st.step) == \
+            (ref.scaler.loss_scale, ref.scaler.good_steps, ref.scaler.step)
+        if kind:
+            for t, b in zip((p, m, v, ag, qb, qs), before):
+                assert_bitwise(to_host(t), b, "skipped step changed state")
+        else:
+            assert_bitwise(to_host(p), ref.p, "master")
+            assert_bitwise(to_host(ag), res["lp"], "slot")
+    assert state.read().loss_scale == ref.scaler.loss_scale
+
+
+def test_tiny_mlp_all_ranks_and_zero_equals_ddp(zf):
+    """2-layer-MLP FlatParameter (1,050,112 params) over 4 simulated ranks,
+    3 steps, fp16 grads reduced with AVG: every rank's shard step equals the
+    oracle bitwise, and the concatenation of the 4 shard updates equals one
+    unsharded (N=1, whole flat buffer) update -- ZeRO == DDP (2kiu.com §5.2)."""
+    from synth.workloads import WORKLOADS, key_grad, key_master
+    w = WORKLOADS["tiny_mlp_n4"]
+    N, S, T = w.n_ranks, w.shard, w.total
+    for max_norm in (1.0, 1e-6):     # clipping off / on (norm ~8e-6)
+        hp = dict(w.hp, max_grad_norm=max_norm)
+        say("tiny all ranks, max_norm", max_norm)
+        master_full = synth.normal_f32(key_master(w), 0, w.padded, w.master_sigma)
+        master_full[T:] = 0
+        opts = [zf.ShardOptimizer(to_dev(master_full[r * S:(r + 1) * S], 0), hp,
+                                  loss_scale=w.loss_scale) for r in range(N)]
+        ddp = zf.ShardOptimizer(to_dev(master_full, 0), hp, loss_scale=w.loss_scale)
+        refs = [OracleRank(master_full[r * S:(r + 1) * S], w.loss_scale, False) for r in range(N)]
+        ag = torch.zeros(w.padded, dtype=torch.float16, device="cuda")
+        ag_ddp = torch.zeros(w.padded, dtype=torch.float16, device="cuda")
+        for step in range(w.steps):
+            grads = []
+            for k in range(N):
+                g = synth.normal_f32(key_grad(w, step, k), 0, w.padded, w.grad_sigma)
+                g[T:] = 0
+                grads.append(synth.to_storage(g, synth.F16))
+            bufs = [to_dev(g, 1) for g in grads]
+            # rank statistics first (the cross-rank sum is the all-reduce stand-in)
+            reds = []
+            for r in range(N):
+                red = opts[r].reduced_buffer()
+                zf.zero_grad_reduce_shard(bufs, r * S, S, zf.ZERO_AVG, red, opts[r].state)
+                reds.append(red)
+            local = [o.state.read().sumsq for o in opts]
+            for r in range(N):
+                opts[r].state.set_remote(sum(local) - local[r], 0)
+                zf.zero_adamw_shard_step(reds[r], opts[r].master, opts[r].exp_avg,
+                                         opts[r].exp_avg_sq, ag, r * S, hp, opts[r].state)
+            ddp.step_from_rank_buffers(bufs, 0, ag_ddp, 0)
+            # oracle, rank by rank
+            ored = [orc.reduce(grads, orc.F16, r * S, S, orc.AVG) for r in range(N)]
+            ostat = [orc.unscale_stats(x, orc.F32, w.loss_scale)[0] for x in ored]
+            for r in range(N):
+                res = refs[r].step(ored[r], orc.F32, hp, orc.F16,
+                                   remote_sumsq=sum(ostat) - ostat[r])
+                assert_bitwise(to_host(opts[r].master), refs[r].p, "rank %d master" % r)
+                assert_bitwise(to_host(opts[r].exp_avg), refs[r].m, "rank %d m" % r)
+                assert_bitwise(to_host(opts[r].exp_avg_sq), refs[r].v, "rank %d v" % r)
+                assert_bitwise(to_host(ag)[r * S:(r + 1) * S], res["lp"], "rank %d slot" % r)
+                st = opts[r].state.read()
+                assert st.last_coef == res["coef"]
+                assert rel(st.last_norm, res["norm"]) <= 1e-5
+            # ZeRO == DDP on the GPU
+            cat = torch.cat([o.master for o in opts])
+            assert_bitwise(to_host(cat), to_host(ddp.master), "ZeRO vs DDP master")
+            assert_bitwise(to_host(ag), to_host(ag_ddp), "ZeRO vs DDP all-gather buffer")
+            assert not to_host(ddp.master)[T:].any(), "padding moved"
+
+
+def test_determinism_and_resume(zf):
+    """Two runs of the same steps give identical bits (norm included), and a
+    run saved after step 2 and resumed equals the uninterrupted run."""
+    n, N = 200_000, 8
+
+    def grads(step):
+        return [to_dev(synth.normal(synth.stream_key("det", step, k), 0, n, 1e-3, 2), 2)
+                for k in range(N)]
+
+    def run(steps, opt=None):
+        opt = opt or zf.ShardOptimizer(to_dev(synth.normal_f32(synth.stream_key("d0"), 0, n,
+                                                                 0.02), 0), HP, loss_scale=1.0)
+        ag = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+        norms = []
+        for s in steps:
+            opt.step_from_rank_buffers(grads(s), 0, ag, 0)
+            norms.append(opt.state.read().last_norm)
+        return opt, ag, norms
+
+    a, ag_a, na = run(range(4))
+    b, ag_b, nb = run(range(4))
+    assert na == nb
+    for x, y in ((a.master, b.master), (a.exp_avg, b.exp_avg), (a.exp_avg_sq, b.exp_avg_sq),
+                 (ag_a, ag_b)):
+        assert torch.equal(x.view(torch.int8) if x.dtype != torch.float32 else x.view(torch.int32),
+                           y.view(torch.int8) if y.dtype != torch.float32 else y.view(torch.int32))
+    c, _, _ = run(range(2))
+    saved = [t.clone() for t in (c.master, c.exp_avg, c.exp_avg_sq)] + [c.state.read()]
+    d = zf.ShardOptimizer(saved[0], HP, loss_scale=1.0)
+    d.exp_avg.copy_(saved[1])
+    d.exp_avg_sq.copy_(saved[2])
+    d.state.upload(saved[3])
+    d, ag_d, nd = run(range(2, 4), d)
+    assert nd == na[2:]
+    assert torch.equal(d.master.view(torch.int32), a.master.view(torch.int32))
+    assert torch.equal(d.exp_avg_sq.view(torch.int32), a.exp_avg_sq.view(torch.int32))
+
+
+def test_bad_arguments_raise(zf):
+    n = 1024
+    p = torch.zeros(n, device="cuda")
+    ag = torch.zeros(n, dtype=torch.float16, device="cuda")
+    state = zf.StepState(1.0, False)
+    with pytest.raises(ValueError):
+        zf.zero_adamw_shard_step(p, p, p, p, ag, 1, HP, state)      # slot past the end
+    with pytest.raises(zf.ZeroError):
+        zf.zero_adamw_shard_step(p, p, p, p, p.view(torch.int32).float(), 0, HP, state)
+    with pytest.raises(ValueError):
+        zf.zero_grad_reduce_shard([ag], 1, n, zf.ZERO_AVG, p, state)
+
+
+@pytest.mark.parametrize("pdt", [1, 2])
+def test_writeback_rounding_exhaustive_cases(zf, pdt):
+    """With lr = wd = 0 and a zero gradient the step leaves the master
+    unchanged, so the slot holds round_nearest_even(master): fed with ties,
+    their neighbours, subnormals, the overflow edge, inf and NaN, plus a
+    strided sweep of all binary32 patterns, it must equal the oracle's
+    rounding bit for bit."""
+    rng = np.random.default_rng(41)
+    sweep = np.arange(0, 1 << 32, 4099, dtype=np.uint64).astype(np.uint32)
+    hi = rng.integers(0, 1 << 16, size=1 << 18, dtype=np.uint64).astype(np.uint32) << 16
+    bf_ties = np.concatenate([hi | 0x8000, hi | 0x7FFF, hi | 0x8001])
+    h = np.arange(0, 0x7C00, dtype=np.uint16)
+    mid = ((h[:-1].view(np.float16).astype(np.float64) + h[1:].view(np.float16).astype(np.float64))
+           / 2).astype(np.float32).view(np.uint32)
+    f16_ties = np.concatenate([mid, mid + 1, mid - 1])
+    special = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 0x477FF000, 0x477FEFFF,
+                        0x38800000, 0x387FFFFF, 0x33000000, 0x33000001, 0x00000001, 0x80000000],
+                       np.uint32)
+    pats = np.concatenate([sweep, bf_ties, f16_ties, f16_ties | 0x80000000, special])
+    n = pats.size - pats.size % 4 + 4
+    pats = np.concatenate([pats, np.zeros(n - pats.size, np.uint32)])
+    x = pats.view(np.float32)
+    p = to_dev(x, 0)
+    z = torch.zeros(n, device="cuda")
+    ag = torch.zeros(n, dtype=torch.float16 if pdt == 1 else torch.bfloat16, device="cuda")
+    state = zf.StepState(1.0, False)
+    zf.zero_adamw_shard_step(z, p, torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda"),
+                             ag, 0, dict(HP, lr=0.0, weight_decay=0.0, max_grad_norm=0.0), state)
+    got = to_host(ag)
+    ref = orc.f32_to_f16(x) if pdt == 1 else orc.f32_to_bf16(x)
+    nan = np.isnan(x)
+    assert_bitwise(got[~nan], ref[~nan], "write-back rounding")
+    assert_bitwise(got[nan], ref[nan], "NaN write-back")
