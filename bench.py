@@ -1,0 +1,261 @@
+"""Benchmark: one rank's sharded mixed-precision AdamW step on one MI355X.
+
+Workload (the 10B-parameter FlatParameter over N=8 ranks, rank 7's shard of
+1.25e9 parameters, slot offset 8.75e9): a pre-reduced fp16 gradient shard
+~N(0,1e-3) is unscaled (static scale 2^16), checked for overflow and reduced
+to the global L2 norm, clipped at 1.0, and the fused AdamW step updates the
+fp32 master/m/v shard and writes the fp16 parameters into the rank's slot of a
+full 20 GB All-Gather buffer.  Inputs are synthetic (seeded, generated on the
+GPU before timing) and resident in HBM when the timed region starts.
+
+A "step" is the whole path: statistics kernel + fold, the AdamW kernel, and
+the loss-scaler finalize.  The AdamW kernel is the dominant one; its duration
+is taken with HIP events on the launch stream around every launch.
+
+Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+ADAM_BYTES_PER_PARAM = {        # algorithmic bytes of one AdamW-kernel launch per parameter
+    "f16": 2 + 12 + 12 + 2,     # grad read, master/m/v read+write, 16-bit slot write
+    "f32": 4 + 12 + 12 + 2,
+}
+KERNEL_SOURCE = os.path.join(ROOT, "fsdp_sharded_mixed_flatparameter_amd", "csrc",
+                             "zeroflat_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_10b_n8_hbm_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the 8-buffer fused-reduce variant")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run the plain copy kernel (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per AdamW launch from the committed rocprofv3 counter runs,
+    or None if they were taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, window=1 << 26, steps=5):
+    """The oracle as it stands, single-threaded, on a window of the same
+    shard (same generator, same hyper-parameters), generation untimed."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    from synth import synth
+    from synth.workloads import key_grad_reduced, key_master
+    start = w.start
+    p = synth.normal_f32(key_master(w), start, window, w.master_sigma, threads=8)
+    m = np.zeros(window, np.float32)
+    v = np.zeros(window, np.float32)
+    grads = [synth.normal(key_grad_reduced(w, s), start, window, w.grad_sigma, w.grad_dtype,
+                          threads=8) for s in range(steps)]
+    sc = orc.make_scaler(w.loss_scale, w.dynamic, w.window)
+    hp = orc.Hparams(**w.hp)
+    t0 = time.perf_counter()
+    for s in range(steps):
+        orc.shard_step(grad=grads[s], grad_dtype=w.grad_dtype, master=p, exp_avg=m,
+                       exp_avg_sq=v, scaler=sc, hp=hp, param_dtype=w.param_dtype)
+    dt = time.perf_counter() - t0
+    return {"value": window * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": "%d-parameter window of the rank-7 shard (elements %d..), %d steps of "
+                      "the oracle's statistics + AdamW + fp16 write-back, one thread; %.1f s"
+                      % (window, start, steps, dt)}
+
+
+def run_prereduced(zf, torch, w, steps, warmup):
+    """The headline workload: pre-reduced fp16 shard -> statistics -> AdamW."""
+    from synth import synth
+    from synth.workloads import key_grad_reduced, key_master
+    S, dev = w.shard, torch.device("cuda:0")
+    f16 = torch.float16
+    master = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_normal(master, key_master(w), w.start, w.master_sigma)
+    opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic)
+    grads = []
+    for s in range(2):   # two distinct pre-reduced gradient shards, alternated
+        g = torch.empty(S, dtype=f16, device=dev)
+        synth.fill_normal(g, key_grad_reduced(w, s), w.start, w.grad_sigma)
+        grads.append(g)
+    ag = torch.zeros(w.padded, dtype=f16, device=dev)      # full 20 GB All-Gather buffer
+    torch.cuda.synchronize()
+
+    ev = []
+
+    def one_step(i, timed):
+        g = grads[i % 2]
+        zf.zero_unscale_norm(g, opt.state)
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        zf.zero_adamw_shard_step(g, opt.master, opt.exp_avg, opt.exp_avg_sq, ag, w.start,
+                                 w.hp, opt.state, finalize=False)
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+        zf.zero_adamw_shard_step(g[:0], opt.master[:0], opt.exp_avg[:0], opt.exp_avg_sq[:0],
+                                 ag, 0, w.hp, opt.state, finalize=True)   # scaler/counters
+
+    for i in range(warmup):
+        one_step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_step(warmup + i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    adam_ms = [a.elapsed_time(b) for a, b in ev]
+    st = opt.state.read()
+    assert st.last_skipped == 0 and st.step == warmup + steps, "unexpected skipped step"
+    res = dict(wall=wall, adam_ms=adam_ms, norm=st.last_norm)
+    del opt, grads, ag, master
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_reduce8(zf, torch, w, steps, warmup):
+    """Variant: the 8 raw fp16 rank slices reduced (AVG) inside the step."""
+    from synth import synth
+    from synth.workloads import key_grad, key_master
+    S, dev = w.shard, torch.device("cuda:0")
+    master = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_normal(master, key_master(w), w.start, w.master_sigma)
+    opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic)
+    bufs = []
+    for k in range(w.n_ranks):      # rank-7 slices of the 8 ranks' full gradient buffers
+        b = torch.empty(S, dtype=torch.float16, device=dev)
+        synth.fill_normal(b, key_grad(w, 0, k), w.start, w.grad_sigma)
+        bufs.append(b)
+    ag = torch.zeros(w.padded, dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        opt.step_from_rank_buffers(bufs, 0, ag, w.start)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        opt.step_from_rank_buffers(bufs, 0, ag, w.start)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del opt, bufs, ag, master
+    torch.cuda.empty_cache()
+    return dict(wall=wall)
+
+
+def run_copy_calibration(torch, nbytes=4 << 30, reps=3):
+    from synth import synth
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        synth.copy(src, dst)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(bytes=2 * nbytes, GBps=2 * nbytes / dt / 1e9)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the rank's step on a single MI355X "
+              "(the other ranks are buffers in the same HBM); --gpus %d is not supported."
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import fsdp_sharded_mixed_flatparameter_amd as zf
+    from synth.workloads import WORKLOADS
+    w = WORKLOADS["10b_n8"]
+    S = w.shard
+
+    copy = run_copy_calibration(torch) if args.calibrate_copy else None
+    res = run_prereduced(zf, torch, w, args.steps, args.warmup)
+    ms_step = res["wall"] / args.steps * 1e3
+    adam_ms = sum(res["adam_ms"]) / len(res["adam_ms"])
+    adam_bytes = ADAM_BYTES_PER_PARAM["f16"] * S
+    achieved = adam_bytes / (adam_ms * 1e-3) / 1e9
+    step_bytes = (2 + ADAM_BYTES_PER_PARAM["f16"]) * S           # + the statistics pass
+    out = {
+        "metric": "sharded AdamW step: params updated/s and achieved HBM GB/s (% of peak) at 1 GPU",
+        "value": S / (ms_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "10b_n8: 10B-param FlatParameter over 8 ranks, rank 7 shard "
+                               "(1.25e9 params), pre-reduced fp16 grads, static loss scale 2^16, "
+                               "clip 1.0, AdamW lr 3e-5 betas (0.9,0.999) eps 1e-8 wd 0.01, fp16 "
+                               "write-back into the full All-Gather buffer at offset 8.75e9",
+                   "shard_params": S, "n_ranks": w.n_ranks, "rank": w.rank,
+                   "parallelism": "one rank's shard on 1 GPU"},
+        "step_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "adamw_kernel (fused AdamW + fp16 write-back)",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": read_traffic(),
+                     "algorithmic_bytes_per_launch": adam_bytes,
+                     "avg_launch_ms": adam_ms},
+    }
+    if copy:
+        out["copy_calibration"] = copy
+    if not args.no_variants:
+        w8 = WORKLOADS["10b_n8_reduce8"]
+        r8 = run_reduce8(zf, torch, w8, max(2, args.steps // 2), 1)
+        ms8 = r8["wall"] / max(2, args.steps // 2) * 1e3
+        b8 = (2 * w8.n_ranks + 4 + ADAM_BYTES_PER_PARAM["f32"]) * S
+        out["variants"] = {"10b_n8_reduce8": {
+            "what": "same shard, 8 raw fp16 rank slices reduced (AVG) in the step",
+            "ms_per_step": ms8, "params_per_s": S / (ms8 * 1e-3),
+            "step_GBps": b8 / (ms8 * 1e-3) / 1e9,
+            "step_frac_of_peak": b8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,9 +12,12 @@
 // elements; in slice u of a tile, lane l holds elements 256u + 4l .. 4l+3, so
 // each fp32 array moves as one 16-byte access per lane (1 KiB per wave
 // instruction) and each 16-bit array as one 8-byte access.  One slice of 256
-// elements is exactly one INT8 block, reduced across the wave.  The reduce
-// kernel instead gives each lane 8 consecutive elements so its dominant
-// 16-bit reads are 16-byte accesses.  Tiles are assigned to waves grid-stride.
+// elements is exactly one INT8 block, reduced across the wave.  All kU
+// slices' loads are issued before any arithmetic (bytes in flight per lane),
+// and every stream uses non-temporal loads/stores: each byte is touched once.
+// By default the grid holds one tile per wave and the hardware dispatcher
+// balances blocks as they retire.  The reduce kernel instead gives each lane 8
+// consecutive elements so its dominant 16-bit reads are 16-byte accesses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,13 +26,50 @@
 namespace zf {
 namespace {
 
+// Launch shape.  ZF_ADAM_U (256-element slices per wave tile) trades bytes in
+// flight per lane against occupancy; ZF_ADAM_GRID caps the AdamW/quant grid
+// (0: one tile per wave, blocks dispatched as earlier ones retire).
+#ifndef ZF_ADAM_U
+#define ZF_ADAM_U 4
+#endif
+#ifndef ZF_ADAM_GRID
+#define ZF_ADAM_GRID 0
+#endif
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kU = 2;                       // 256-element slices per adamw/quant tile
+constexpr int kU = ZF_ADAM_U;               // 256-element slices per adamw/quant tile
 constexpr int64_t kTile = 256 * kU;         // adamw/quant tile (elements per wave)
-constexpr int64_t kRTile = 512;             // reduce tile: 8 elements per lane
-constexpr int kMaxGridStep = 4096;          // adamw grid cap (blocks)
+constexpr int kMaxGridStep = ZF_ADAM_GRID > 0 ? ZF_ADAM_GRID : 0x7fffffff;
 constexpr int kMaxGridReduce = ZERO_MAX_PARTIALS;
+
+// Native vectors for the non-temporal (streaming, read-once / write-once)
+// accesses: every array of the step is touched exactly once per launch.
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f ldnt_f4(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+}
+__device__ __forceinline__ void stnt_f4(float* p, float a, float b, float c, float d) {
+    v4f x;
+    x.x = a; x.y = b; x.z = c; x.w = d;
+    __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(p));
+}
+__device__ __forceinline__ v2u ldnt_u2(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+}
+__device__ __forceinline__ void stnt_u2(void* p, uint32_t a, uint32_t b) {
+    v2u x;
+    x.x = a; x.y = b;
+    __builtin_nontemporal_store(x, reinterpret_cast<v2u*>(p));
+}
+__device__ __forceinline__ v4u ldnt_u4(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+}
+__device__ __forceinline__ void stnt_u1(void* p, uint32_t a) {
+    __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
+}
 
 // ---------------------------------------------------------------- formats
 __device__ __forceinline__ float h2f(uint32_t h) {
@@ -80,10 +120,10 @@ __device__ __forceinline__ float load_one(const void* p, int64_t i) {
 template <int DT>
 __device__ __forceinline__ void load_quad(const void* p, int64_t i, float out[4]) {
     if constexpr (DT == ZERO_F32) {
-        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+        const v4f f = ldnt_f4(static_cast<const float*>(p) + i);
         out[0] = f.x; out[1] = f.y; out[2] = f.z; out[3] = f.w;
     } else {
-        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        const v2u w = ldnt_u2(static_cast<const uint16_t*>(p) + i);
         out[0] = cvt16<DT>(w.x & 0xffffu);
         out[1] = cvt16<DT>(w.x >> 16);
         out[2] = cvt16<DT>(w.y & 0xffffu);
@@ -148,108 +188,148 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // statistics of u = red * (1/loss_scale): per-block fp64 partial of u^2 into
 // st->partials[block] and an overflow flag.  A fold kernel adds the partials
 // into st->sumsq in a fixed order, so the sum is reproducible.
-template <int DT, bool VEC, bool WRITE, bool STATS>
+//
+// Mapping: a lane owns 8 consecutive elements of each 512-element chunk (one
+// 16-byte read per 16-bit buffer, 1 KiB per wave instruction); a wave takes
+// TU chunks per iteration so that the one-buffer statistics pass still has
+// TU reads in flight per lane; with many buffers, KC buffers' reads are
+// issued together before they are added (in rank order per element).
+template <int DT, bool VEC, bool WRITE, bool STATS, int TU>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float inv_n,
                                                           int pow2_n) {
+    constexpr int64_t kT = 512 * TU;
     const int lane = threadIdx.x & 63;
     const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const int64_t n = a.n;
     const int N = a.n_ranks;
+    const bool avg = a.op == ZERO_AVG;
     float inv_scale = 1.0f;
     if constexpr (STATS) inv_scale = (float)(1.0 / (double)a.st->loss_scale);
     const float fN = (float)N;
 
-    double ss = 0.0;
-    int ovf = 0;
-    const int64_t ntiles = (n + kRTile - 1) / kRTile;
-    const int64_t nfull = VEC ? n / kRTile : 0;
+    // Sum of u^2 in two fixed-order binary64 chains (even / odd element of each
+    // pair).  u*u is exact in binary64, so fma(u, u, s) equals s + u*u rounded
+    // once.  No term can overflow binary64 (|u| < 2^128) and squares are >= 0,
+    // so the sum is non-finite exactly when some u is inf or NaN: that is the
+    // overflow test, taken once per lane after the loop.
+    double ss0 = 0.0, ss1 = 0.0;
+    const int64_t ntiles = (n + kT - 1) / kT;
+    const int64_t nfull = VEC ? n / kT : 0;
     for (int64_t t = wave_id; t < ntiles; t += nwaves) {
-        const int64_t i0 = t * kRTile + 8 * lane;
-        float acc[8];
+        const int64_t base = t * kT + 8 * lane;
+        float acc[TU][8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+        for (int j = 0; j < TU; ++j)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[j][c] = 0.0f;
         const bool full = t < nfull;
         if (full) {
             if constexpr (DT == ZERO_F32) {
                 for (int k = 0; k < N; ++k) {
-                    const float* b = static_cast<const float*>(a.bufs[k]) + i0;
-                    const float4 x0 = reinterpret_cast<const float4*>(b)[0];
-                    const float4 x1 = reinterpret_cast<const float4*>(b)[1];
-                    acc[0] = acc[0] + x0.x; acc[1] = acc[1] + x0.y;
-                    acc[2] = acc[2] + x0.z; acc[3] = acc[3] + x0.w;
-                    acc[4] = acc[4] + x1.x; acc[5] = acc[5] + x1.y;
-                    acc[6] = acc[6] + x1.z; acc[7] = acc[7] + x1.w;
+                    const float* b = static_cast<const float*>(a.bufs[k]) + base;
+                    v4f x[TU][2];
+#pragma unroll
+                    for (int j = 0; j < TU; ++j) {
+                        x[j][0] = ldnt_f4(b + 512 * j);
+                        x[j][1] = ldnt_f4(b + 512 * j + 4);
+                    }
+#pragma unroll
+                    for (int j = 0; j < TU; ++j) {
+                        acc[j][0] = acc[j][0] + x[j][0].x; acc[j][1] = acc[j][1] + x[j][0].y;
+                        acc[j][2] = acc[j][2] + x[j][0].z; acc[j][3] = acc[j][3] + x[j][0].w;
+                        acc[j][4] = acc[j][4] + x[j][1].x; acc[j][5] = acc[j][5] + x[j][1].y;
+                        acc[j][6] = acc[j][6] + x[j][1].z; acc[j][7] = acc[j][7] + x[j][1].w;
+                    }
                 }
             } else {
-                constexpr int KC = 8;  // buffers whose loads are issued together
+                constexpr int KC = TU >= 4 ? 1 : 8 / TU;  // buffers whose reads issue together
                 int k = 0;
                 for (; k + KC <= N; k += KC) {
-                    uint4 w[KC];
+                    v4u w[KC][TU];
 #pragma unroll
-                    for (int j = 0; j < KC; ++j)
-                        w[j] = *reinterpret_cast<const uint4*>(
-                            static_cast<const uint16_t*>(a.bufs[k + j]) + i0);
+                    for (int kk = 0; kk < KC; ++kk)
 #pragma unroll
-                    for (int j = 0; j < KC; ++j) {  // rank order per element
-                        acc[0] = acc[0] + cvt16<DT>(w[j].x & 0xffffu);
-                        acc[1] = acc[1] + cvt16<DT>(w[j].x >> 16);
-                        acc[2] = acc[2] + cvt16<DT>(w[j].y & 0xffffu);
-                        acc[3] = acc[3] + cvt16<DT>(w[j].y >> 16);
-                        acc[4] = acc[4] + cvt16<DT>(w[j].z & 0xffffu);
-                        acc[5] = acc[5] + cvt16<DT>(w[j].z >> 16);
-                        acc[6] = acc[6] + cvt16<DT>(w[j].w & 0xffffu);
-                        acc[7] = acc[7] + cvt16<DT>(w[j].w >> 16);
+                        for (int j = 0; j < TU; ++j)
+                            w[kk][j] = ldnt_u4(static_cast<const uint16_t*>(a.bufs[k + kk]) +
+                                               base + 512 * j);
+#pragma unroll
+                    for (int kk = 0; kk < KC; ++kk) {  // rank order per element
+#pragma unroll
+                        for (int j = 0; j < TU; ++j) {
+                            acc[j][0] = acc[j][0] + cvt16<DT>(w[kk][j].x & 0xffffu);
+                            acc[j][1] = acc[j][1] + cvt16<DT>(w[kk][j].x >> 16);
+                            acc[j][2] = acc[j][2] + cvt16<DT>(w[kk][j].y & 0xffffu);
+                            acc[j][3] = acc[j][3] + cvt16<DT>(w[kk][j].y >> 16);
+                            acc[j][4] = acc[j][4] + cvt16<DT>(w[kk][j].z & 0xffffu);
+                            acc[j][5] = acc[j][5] + cvt16<DT>(w[kk][j].z >> 16);
+                            acc[j][6] = acc[j][6] + cvt16<DT>(w[kk][j].w & 0xffffu);
+                            acc[j][7] = acc[j][7] + cvt16<DT>(w[kk][j].w >> 16);
+                        }
                     }
                 }
                 for (; k < N; ++k) {
-                    const uint4 w = *reinterpret_cast<const uint4*>(
-                        static_cast<const uint16_t*>(a.bufs[k]) + i0);
-                    acc[0] = acc[0] + cvt16<DT>(w.x & 0xffffu);
-                    acc[1] = acc[1] + cvt16<DT>(w.x >> 16);
-                    acc[2] = acc[2] + cvt16<DT>(w.y & 0xffffu);
-                    acc[3] = acc[3] + cvt16<DT>(w.y >> 16);
-                    acc[4] = acc[4] + cvt16<DT>(w.z & 0xffffu);
-                    acc[5] = acc[5] + cvt16<DT>(w.z >> 16);
-                    acc[6] = acc[6] + cvt16<DT>(w.w & 0xffffu);
-                    acc[7] = acc[7] + cvt16<DT>(w.w >> 16);
+                    v4u w[TU];
+#pragma unroll
+                    for (int j = 0; j < TU; ++j)
+                        w[j] = ldnt_u4(static_cast<const uint16_t*>(a.bufs[k]) + base + 512 * j);
+#pragma unroll
+                    for (int j = 0; j < TU; ++j) {
+                        acc[j][0] = acc[j][0] + cvt16<DT>(w[j].x & 0xffffu);
+                        acc[j][1] = acc[j][1] + cvt16<DT>(w[j].x >> 16);
+                        acc[j][2] = acc[j][2] + cvt16<DT>(w[j].y & 0xffffu);
+                        acc[j][3] = acc[j][3] + cvt16<DT>(w[j].y >> 16);
+                        acc[j][4] = acc[j][4] + cvt16<DT>(w[j].z & 0xffffu);
+                        acc[j][5] = acc[j][5] + cvt16<DT>(w[j].z >> 16);
+                        acc[j][6] = acc[j][6] + cvt16<DT>(w[j].w & 0xffffu);
+                        acc[j][7] = acc[j][7] + cvt16<DT>(w[j].w >> 16);
+                    }
                 }
             }
         } else {
             for (int k = 0; k < N; ++k) {
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    if (i0 + c < n) acc[c] = acc[c] + load_one<DT>(a.bufs[k], i0 + c);
+                for (int j = 0; j < TU; ++j)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const int64_t i = base + 512 * j + c;
+                        if (i < n) acc[j][c] = acc[j][c] + load_one<DT>(a.bufs[k], i);
+                    }
             }
         }
-        float red[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            red[c] = a.op != ZERO_AVG ? acc[c] : (pow2_n ? acc[c] * inv_n : acc[c] / fN);
-        if constexpr (WRITE) {
-            if (full) {
-                float4* o = reinterpret_cast<float4*>(a.red_out + i0);
-                o[0] = make_float4(red[0], red[1], red[2], red[3]);
-                o[1] = make_float4(red[4], red[5], red[6], red[7]);
-            } else {
+        for (int j = 0; j < TU; ++j) {
+            const int64_t i0 = base + 512 * j;
+            float red[8];
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    if (i0 + c < n) a.red_out[i0 + c] = red[c];
+            for (int c = 0; c < 8; ++c)
+                red[c] = !avg ? acc[j][c] : (pow2_n ? acc[j][c] * inv_n : acc[j][c] / fN);
+            if constexpr (WRITE) {
+                if (full) {
+                    stnt_f4(a.red_out + i0, red[0], red[1], red[2], red[3]);
+                    stnt_f4(a.red_out + i0 + 4, red[4], red[5], red[6], red[7]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+                        if (i0 + c < n) a.red_out[i0 + c] = red[c];
+                }
             }
-        }
-        if constexpr (STATS) {
+            if constexpr (STATS) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if (full || i0 + c < n) {
-                    const float u = red[c] * inv_scale;
-                    ovf |= !isfinite(u);
-                    ss = ss + (double)u * (double)u;
+                for (int c = 0; c < 8; ++c) {
+                    if (full || i0 + c < n) {
+                        const double u = (double)(red[c] * inv_scale);
+                        if (c & 1) ss1 = __builtin_fma(u, u, ss1);
+                        else ss0 = __builtin_fma(u, u, ss0);
+                    }
                 }
             }
         }
     }
     if constexpr (STATS) {
-        const double bs = block_sum(ss);
+        const double mine = ss0 + ss1;
+        const int ovf = !isfinite(mine);
+        const double bs = block_sum(mine);
         if (threadIdx.x == 0) {
             a.st->partials[blockIdx.x] = bs;
             if (blockIdx.x == 0) a.st->n_partials = (int32_t)gridDim.x;
@@ -339,11 +419,10 @@ __device__ __forceinline__ void adam_tile(const AdamLaunch& a, const StepScalars
         }
         uint16_t* lp = static_cast<uint16_t*>(a.lp);
         if constexpr (FULL) {
-            *reinterpret_cast<float4*>(a.p + i0) = make_float4(pv[u][0], pv[u][1], pv[u][2], pv[u][3]);
-            *reinterpret_cast<float4*>(a.m + i0) = make_float4(mv[u][0], mv[u][1], mv[u][2], mv[u][3]);
-            *reinterpret_cast<float4*>(a.v + i0) = make_float4(vv[u][0], vv[u][1], vv[u][2], vv[u][3]);
-            *reinterpret_cast<uint2*>(lp + i0) =
-                make_uint2(lp16[0] | (lp16[1] << 16), lp16[2] | (lp16[3] << 16));
+            stnt_f4(a.p + i0, pv[u][0], pv[u][1], pv[u][2], pv[u][3]);
+            stnt_f4(a.m + i0, mv[u][0], mv[u][1], mv[u][2], mv[u][3]);
+            stnt_f4(a.v + i0, vv[u][0], vv[u][1], vv[u][2], vv[u][3]);
+            stnt_u2(lp + i0, lp16[0] | (lp16[1] << 16), lp16[2] | (lp16[3] << 16));
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -361,7 +440,7 @@ __device__ __forceinline__ void adam_tile(const AdamLaunch& a, const StepScalars
             float scale;
             const uint32_t q = quant_quad(lpv, &scale);  // whole wave takes part
             if constexpr (FULL) {
-                *reinterpret_cast<uint32_t*>(a.q + i0) = q;
+                stnt_u1(a.q + i0, q);
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -442,7 +521,7 @@ __global__ void __launch_bounds__(kThreads) quant_kernel(QuantLaunch a) {
             float scale;
             const uint32_t q = quant_quad(x, &scale);
             if (full) {
-                *reinterpret_cast<uint32_t*>(a.q + i0) = q;
+                stnt_u1(a.q + i0, q);
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -464,13 +543,20 @@ int grid_for_tiles(int64_t ntiles, int cap) {
 
 template <int DT, bool VEC, bool WRITE, bool STATS>
 int launch_reduce_t(const ReduceLaunch& a, void* stream) {
-    const int64_t ntiles = (a.n + kRTile - 1) / kRTile;
-    const int grid = grid_for_tiles(ntiles, kMaxGridReduce);
     const int N = a.n_ranks;
     const int pow2 = (N & (N - 1)) == 0;
     const float inv_n = 1.0f / (float)N;  // exact when N is a power of two
-    hipLaunchKernelGGL((reduce_kernel<DT, VEC, WRITE, STATS>), dim3(grid), dim3(kThreads), 0,
-                       (hipStream_t)stream, a, inv_n, pow2);
+    if (N <= 2) {   // few buffers: 4 chunks per lane keep reads in flight
+        const int64_t ntiles = (a.n + 2048 - 1) / 2048;
+        const int grid = grid_for_tiles(ntiles, kMaxGridReduce);
+        hipLaunchKernelGGL((reduce_kernel<DT, VEC, WRITE, STATS, 4>), dim3(grid), dim3(kThreads),
+                           0, (hipStream_t)stream, a, inv_n, pow2);
+    } else {
+        const int64_t ntiles = (a.n + 512 - 1) / 512;
+        const int grid = grid_for_tiles(ntiles, kMaxGridReduce);
+        hipLaunchKernelGGL((reduce_kernel<DT, VEC, WRITE, STATS, 1>), dim3(grid), dim3(kThreads),
+                           0, (hipStream_t)stream, a, inv_n, pow2);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (STATS) {

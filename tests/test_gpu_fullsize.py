@@ -1,0 +1,297 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark uses.  The GPU fills its tensors with the device copy of the seeded
+generator; the oracle regenerates, on the host, exactly the elements it checks
+(the generator is random-access by global flat index):
+
+- sampled elements (random indices plus both ends of the shard and tile
+  boundaries) are followed through every step by the oracle and compared bit
+  for bit (master, m, v, the 16-bit slot, INT8 codes and scales of whole
+  sampled blocks);
+- the global norm of a step is recomputed by the oracle over the whole shard
+  (chunks on host threads, each chunk summed by the oracle, chunk sums added in
+  order) and compared at 1e-5;
+- where the clip coefficient does not depend on the exact norm, that is shown
+  by a bound that holds at any size (generator values are bounded by 6 sigma).
+"""
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+from harness import OracleRank, assert_bitwise, to_dev, to_host
+from oracle import oracle as orc
+from synth import synth
+from synth.workloads import WORKLOADS, key_grad, key_grad_reduced, key_master
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 4)
+CHUNK = 1 << 24
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def zf():
+    import fsdp_sharded_mixed_flatparameter_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def sample_indices(S, n_random=40_000, seed=0):
+    rng = np.random.default_rng(seed)
+    ends = np.concatenate([np.arange(0, 1024), np.arange(S - 1024, S)])
+    tiles = np.arange(0, S, 1 << 20)[:2000]
+    idx = np.unique(np.concatenate([rng.integers(0, S, n_random), ends, tiles, tiles - 1]))
+    return idx[(idx >= 0) & (idx < S)].astype(np.int64)
+
+
+def gather(t, idx):
+    return to_host(t[torch.from_numpy(idx).to(t.device)])
+
+
+def coef_is_one_by_bound(w, n_elems, scale):
+    """||u|| <= max|u| * sqrt(n): with |x| <= 6 sigma (generator bound, plus
+    one 16-bit rounding) the clip coefficient is exactly 1 whenever that bound
+    is below max_norm - 1e-6."""
+    max_u = 6.0 * w.grad_sigma * (1 + 2.0 ** -8) / scale
+    return max_u * math.sqrt(n_elems) < w.hp["max_grad_norm"] - 1e-6
+
+
+def full_sumsq_prereduced(w, step, scale):
+    """Oracle sum of squares over the whole pre-reduced shard."""
+    S, start = w.shard, w.start
+
+    def job(lo):
+        n = min(CHUNK, S - lo)
+        g = synth.normal(key_grad_reduced(w, step), start + lo, n, w.grad_sigma, w.grad_dtype)
+        return orc.unscale_stats(g, w.grad_dtype, scale)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(job, range(0, S, CHUNK)))
+    return sum(p[0] for p in parts), int(any(p[1] for p in parts))
+
+
+def full_sumsq_reduce(w, step, scale, chunk=1 << 20):
+    S, start, N = w.shard, w.start, w.n_ranks
+
+    def job(lo):
+        n = min(chunk, S - lo)
+        bufs = [rank_grad_range(w, step, k, start + lo, n) for k in range(N)]
+        red = orc.reduce(bufs, w.grad_dtype, 0, n, w.op)
+        return orc.unscale_stats(red, orc.F32, scale)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(job, range(0, S, chunk)))
+    return sum(p[0] for p in parts), int(any(p[1] for p in parts))
+
+
+def rank_grad_range(w, step, k, j0, n):
+    """Rank k's gradient over flat [j0, j0+n): zero past the real parameters."""
+    x = synth.normal_f32(key_grad(w, step, k), j0, n, w.grad_sigma)
+    x[max(0, w.total - j0):] = 0.0
+    return synth.to_storage(x, w.grad_dtype)
+
+
+def rank_grad_at(w, step, k, flat_idx):
+    x = synth.normal_f32_at(key_grad(w, step, k), flat_idx, w.grad_sigma)
+    x[flat_idx >= w.total] = 0.0
+    return synth.to_storage(x, w.grad_dtype)
+
+
+def master_at(w, flat_idx):
+    x = synth.normal_f32_at(key_master(w), flat_idx, w.master_sigma)
+    x[flat_idx >= w.total] = 0.0
+    return x
+
+
+# ------------------------------------------------------------------ 10B over 8 ranks
+def test_10b_n8_rank7_full_size(zf):
+    w = WORKLOADS["10b_n8"]
+    S, start = w.shard, w.start
+    say("10b_n8: shard", S, "slot offset", start)
+    dev = torch.device("cuda:0")
+    master = torch.empty(S, device=dev)
+    synth.fill_normal(master, key_master(w), start, w.master_sigma)
+    opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic)
+    ag = torch.zeros(w.padded, dtype=torch.float16, device=dev)
+    g = torch.empty(S, dtype=torch.float16, device=dev)
+    idx = sample_indices(S)
+    ref = OracleRank(master_at(w, start + idx), w.loss_scale, w.dynamic)
+    assert coef_is_one_by_bound(w, S, w.loss_scale)
+    for step in range(w.steps):
+        say("10b_n8 step", step)
+        synth.fill_normal(g, key_grad_reduced(w, step), start, w.grad_sigma)
+        opt.step_from_reduced(g, ag, start)
+        st = opt.state.read()
+        gs = synth.normal_at(key_grad_reduced(w, step), start + idx, w.grad_sigma, w.grad_dtype)
+        if step in (0, w.steps - 1):
+            sumsq, ovf = full_sumsq_prereduced(w, step, w.loss_scale)
+            assert ovf == 0 and abs(st.last_norm - math.sqrt(sumsq)) <= 1e-5 * math.sqrt(sumsq)
+        else:
+            # the norm enters the update only through coef, which the bound fixes at
+            # exactly 1: any sum below the bound stands for it
+            sumsq, ovf = 0.0, 0
+        res = ref.step(gs, w.grad_dtype, w.hp, w.param_dtype, sumsq_local=sumsq,
+                       overflow_local=ovf)
+        assert res["coef"] == 1.0 and st.last_coef == 1.0 and st.last_skipped == 0
+        assert_bitwise(gather(opt.master, idx), ref.p, "master step %d" % step)
+        assert_bitwise(gather(opt.exp_avg, idx), ref.m, "exp_avg step %d" % step)
+        assert_bitwise(gather(opt.exp_avg_sq, idx), ref.v, "exp_avg_sq step %d" % step)
+        assert_bitwise(gather(ag, start + idx), res["lp"], "slot step %d" % step)
+    # nothing outside rank 7's slot was written (its neighbours' slots stay zero)
+    assert not ag[start - (1 << 20):start].any() and not ag[:1 << 20].any()
+    assert st.step == w.steps
+    del opt, ag, g, master
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ 70B over 64 ranks, INT8
+def test_70b_n64_rank63_int8_full_size(zf):
+    w = WORKLOADS["70b_n64_int8"]
+    S, start = w.shard, w.start
+    nb = -(-S // 256)
+    say("70b_n64_int8: shard", S, "blocks", nb, "last block", S - (nb - 1) * 256)
+    dev = torch.device("cuda:0")
+    master = torch.empty(S, device=dev)
+    synth.fill_normal(master, key_master(w), start, w.master_sigma)
+    opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic,
+                            quant_block=256)
+    slot = torch.zeros(S, dtype=torch.bfloat16, device=dev)   # slot-sized buffer
+    q = torch.zeros(S, dtype=torch.int8, device=dev)
+    qs = torch.zeros(nb, device=dev)
+    g = torch.empty(S, dtype=torch.bfloat16, device=dev)
+    rng = np.random.default_rng(5)
+    blocks = np.unique(np.concatenate([rng.integers(0, nb, 150), [0, 1, nb - 2, nb - 1]]))
+    idx = np.concatenate([np.arange(b * 256, min((b + 1) * 256, S)) for b in blocks])
+    ref = OracleRank(master_at(w, start + idx), w.loss_scale, w.dynamic)
+    for step in range(w.steps):
+        say("70b step", step)
+        synth.fill_normal(g, key_grad_reduced(w, step), start, w.grad_sigma)
+        opt.step_from_reduced(g, slot, 0, q_buf=q, q_scales=qs)
+        st = opt.state.read()
+        sumsq, ovf = full_sumsq_prereduced(w, step, w.loss_scale)
+        assert ovf == 0
+        assert abs(st.last_norm - math.sqrt(sumsq)) <= 1e-5 * math.sqrt(sumsq)
+        gs = synth.normal_at(key_grad_reduced(w, step), start + idx, w.grad_sigma, w.grad_dtype)
+        res = ref.step(gs, w.grad_dtype, w.hp, w.param_dtype, sumsq_local=sumsq,
+                       overflow_local=ovf)
+        assert res["coef"] < 0.1, "clipping must be active"
+        assert st.last_coef == res["coef"]
+        assert_bitwise(gather(opt.master, idx), ref.p, "master step %d" % step)
+        assert_bitwise(gather(opt.exp_avg, idx), ref.m, "exp_avg step %d" % step)
+        assert_bitwise(gather(opt.exp_avg_sq, idx), ref.v, "exp_avg_sq step %d" % step)
+        lp = gather(slot, idx)
+        assert_bitwise(lp, res["lp"], "bf16 slot step %d" % step)
+        # INT8 of each sampled block, from the oracle's written values
+        pos = 0
+        for b in blocks:
+            n_b = min((b + 1) * 256, S) - b * 256
+            rq, rs = orc.quant_int8(np.ascontiguousarray(res["lp"][pos:pos + n_b]), orc.BF16, 256)
+            assert_bitwise(gather(q, np.arange(b * 256, b * 256 + n_b)).view(np.uint8),
+                           rq.view(np.uint8), "int8 block %d step %d" % (b, step))
+            assert to_host(qs[int(b):int(b) + 1])[0] == rs[0]
+            pos += n_b
+    del opt, slot, q, qs, g, master
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ Llama-style 7B block, bf16, overflow
+@pytest.mark.parametrize("op", [1, 0])
+def test_llama7b_block_rank3_overflow_full_size(zf, op):
+    """Full oracle over the whole 25,297,920-element shard.  Step 2 carries an
+    injected +inf in buffer 5 inside rank 3's slice: the step is skipped
+    (state bitwise unchanged), the scale halves; step 3 runs at 2^15."""
+    w = WORKLOADS["llama7b_block_n8"]
+    S, start, N = w.shard, w.start, w.n_ranks
+    steps = w.steps if op == 1 else 2
+    say("llama7b block op", op, "shard", S, "start", start)
+    dev = torch.device("cuda:0")
+    master0 = synth.normal_f32(key_master(w), start, S, w.master_sigma, threads=THREADS)
+    opt = zf.ShardOptimizer(to_dev(master0, 0), w.hp, loss_scale=w.loss_scale,
+                            dynamic=w.dynamic, window=w.window)
+    ref = OracleRank(master0, w.loss_scale, w.dynamic, w.window)
+    ag = torch.zeros(w.padded, dtype=torch.bfloat16, device=dev)
+    bufs = [torch.empty(w.padded, dtype=torch.bfloat16, device=dev) for _ in range(N)]
+    for step in range(steps):
+        say("llama7b step", step)
+        host = []
+        for k in range(N):            # full padded buffers on the GPU; rank-3 slices on the host
+            synth.fill_normal(bufs[k][:w.total], key_grad(w, step, k), 0, w.grad_sigma)
+            bufs[k][w.total:].zero_()
+            host.append(synth.normal(key_grad(w, step, k), start, S, w.grad_sigma, w.grad_dtype,
+                                     threads=THREADS))
+        inject = w.inject is not None and w.inject[0] == step
+        if inject:
+            _, kb, flat, val = w.inject
+            bufs[kb][flat] = val
+            host[kb][flat - start] = synth.to_storage(np.array([val], np.float32), w.grad_dtype)[0]
+        before = [to_host(t).copy() for t in (opt.master, opt.exp_avg, opt.exp_avg_sq)]
+        ag_before = to_host(ag[start:start + S]).copy()
+        opt.step_from_rank_buffers(bufs, start, ag, start, op=op)
+        red = orc.reduce(host, w.grad_dtype, 0, S, op)
+        res = ref.step(red, orc.F32, w.hp, w.param_dtype)
+        st = opt.state.read()
+        assert st.last_skipped == res["skipped"] == int(inject)
+        assert (st.loss_scale, st.good_steps, st.step) == \
+            (ref.scaler.loss_scale, ref.scaler.good_steps, ref.scaler.step)
+        if inject:
+            for t, b in zip((opt.master, opt.exp_avg, opt.exp_avg_sq), before):
+                assert_bitwise(to_host(t), b, "skipped step moved the state")
+            assert_bitwise(to_host(ag[start:start + S]), ag_before, "skipped step wrote the slot")
+            assert st.loss_scale == w.loss_scale / 2
+            continue
+        assert abs(st.last_norm - res["norm"]) <= 1e-5 * res["norm"]
+        assert st.last_coef == res["coef"]
+        assert_bitwise(to_host(opt.master), ref.p, "master step %d" % step)
+        assert_bitwise(to_host(opt.exp_avg), ref.m, "exp_avg step %d" % step)
+        assert_bitwise(to_host(opt.exp_avg_sq), ref.v, "exp_avg_sq step %d" % step)
+        assert_bitwise(to_host(ag[start:start + S]), res["lp"], "slot step %d" % step)
+    assert not ag[:start].any() and not ag[start + S:].any()
+    del opt, ag, bufs
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ 1.5B over 64 ranks
+def test_gpt1p5b_n64_rank0_full_size(zf):
+    """64 fp16 rank slices reduced with AVG, dynamic scale, 10 steps."""
+    w = WORKLOADS["gpt1p5b_n64"]
+    S, start, N = w.shard, w.start, w.n_ranks
+    say("gpt1p5b: shard", S, "ranks", N)
+    dev = torch.device("cuda:0")
+    master = torch.empty(S, device=dev)
+    synth.fill_normal(master, key_master(w), start, w.master_sigma)
+    opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic,
+                            window=w.window)
+    ag = torch.zeros(w.padded, dtype=torch.float16, device=dev)
+    slices = [torch.empty(S, dtype=torch.float16, device=dev) for _ in range(N)]
+    idx = sample_indices(S, 20_000, seed=3)
+    ref = OracleRank(master_at(w, start + idx), w.loss_scale, w.dynamic, w.window)
+    assert coef_is_one_by_bound(w, S, w.loss_scale)
+    for step in range(w.steps):
+        say("gpt1p5b step", step)
+        for k in range(N):
+            synth.fill_normal(slices[k], key_grad(w, step, k), start, w.grad_sigma)
+        opt.step_from_rank_buffers(slices, 0, ag, start)
+        st = opt.state.read()
+        if step == 0:
+            sumsq, ovf = full_sumsq_reduce(w, step, w.loss_scale)
+            assert ovf == 0 and abs(st.last_norm - math.sqrt(sumsq)) <= 1e-5 * math.sqrt(sumsq)
+        else:
+            sumsq, ovf = 0.0, 0   # enters only through coef, fixed at 1 by the bound
+        hb = [rank_grad_at(w, step, k, start + idx) for k in range(N)]
+        red = orc.reduce(hb, w.grad_dtype, 0, idx.size, w.op)
+        res = ref.step(red, orc.F32, w.hp, w.param_dtype, sumsq_local=sumsq, overflow_local=ovf)
+        assert res["coef"] == 1.0 == st.last_coef and st.last_skipped == 0
+        assert_bitwise(gather(opt.master, idx), ref.p, "master step %d" % step)
+        assert_bitwise(gather(opt.exp_avg, idx), ref.m, "exp_avg step %d" % step)
+        assert_bitwise(gather(opt.exp_avg_sq, idx), ref.v, "exp_avg_sq step %d" % step)
+        assert_bitwise(gather(ag, start + idx), res["lp"], "slot step %d" % step)
+    assert st.loss_scale == 65536.0 and st.step == w.steps and st.good_steps == w.steps
+    del opt, ag, slices, master
+    torch.cuda.empty_cache()
