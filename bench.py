@@ -32,6 +32,15 @@ ADAM_BYTES_PER_PARAM = {        # algorithmic bytes of one AdamW-kernel launch p
 KERNEL_SOURCE = os.path.join(ROOT, "fsdp_sharded_mixed_flatparameter_amd", "csrc",
                              "zeroflat_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_10b_n8_hbm_traffic.txt")
+VARIANTS = (   # the other workloads, whole steps each (parity cases in tests/ as well)
+    ("10b_n8_reduce8", "10B/8 rank-7 shard with the 8 raw fp16 rank slices reduced (AVG) in the step"),
+    ("70b_n64_int8", "70B/64 rank-63 shard (1.09e9), pre-reduced bf16, clipping active, bf16 "
+                     "write-back + INT8 blocks of 256"),
+    ("gpt1p5b_n64", "1.5B/64 rank-0 shard (2.34e7), 64 fp16 rank slices reduced (AVG), dynamic scale"),
+    ("llama7b_block_n8", "Llama-7B block (2.02e8 params)/8 rank-3 shard, 8 bf16 rank slices (AVG)"),
+    ("tiny_mlp_n4", "2-layer MLP (1.05e6 params)/4 rank-0 shard, 4 fp16 rank slices (AVG); "
+                    "cache-resident and launch-bound"),
+)
 
 
 def parse():
@@ -41,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the 8-buffer fused-reduce variant")
+                    help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run the plain copy kernel (counter calibration)")
     return ap.parse_args()
@@ -148,32 +157,75 @@ def run_prereduced(zf, torch, w, steps, warmup):
     return res
 
 
-def run_reduce8(zf, torch, w, steps, warmup):
-    """Variant: the 8 raw fp16 rank slices reduced (AVG) inside the step."""
+def step_bytes_per_param(w):
+    """Algorithmic HBM bytes of one whole step per shard parameter."""
+    g16 = 2
+    if w.reduce:
+        stats_and_reduce = g16 * w.n_ranks + 4          # N reads, fp32 reduced shard written
+        adam_grad = 4                                   # the fp32 reduced shard read back
+    else:
+        stats_and_reduce = g16                          # statistics pass over the 16-bit shard
+        adam_grad = g16
+    b = stats_and_reduce + adam_grad + 12 + 12 + 2      # master/m/v read+write, 16-bit slot
+    if w.quant_block:
+        b += 1 + 4.0 / w.quant_block                    # INT8 codes + one fp32 scale per block
+    return b
+
+
+def run_workload(zf, torch, w, steps, warmup):
+    """Whole steps of any workload (inputs generated on the GPU first)."""
     from synth import synth
-    from synth.workloads import key_grad, key_master
+    from synth.workloads import key_grad, key_grad_reduced, key_master
     S, dev = w.shard, torch.device("cuda:0")
+    gdt = torch.float16 if w.grad_dtype == 1 else torch.bfloat16
+    pdt = torch.float16 if w.param_dtype == 1 else torch.bfloat16
     master = torch.empty(S, dtype=torch.float32, device=dev)
     synth.fill_normal(master, key_master(w), w.start, w.master_sigma)
-    opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic)
-    bufs = []
-    for k in range(w.n_ranks):      # rank-7 slices of the 8 ranks' full gradient buffers
-        b = torch.empty(S, dtype=torch.float16, device=dev)
-        synth.fill_normal(b, key_grad(w, 0, k), w.start, w.grad_sigma)
-        bufs.append(b)
-    ag = torch.zeros(w.padded, dtype=torch.float16, device=dev)
+    opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic,
+                            window=w.window, quant_block=w.quant_block)
+    if w.reduce:
+        # rank-r slices of the N ranks' gradient buffers (slot-sized, offset 0)
+        grads = []
+        for k in range(w.n_ranks):
+            b = torch.empty(S, dtype=gdt, device=dev)
+            synth.fill_normal(b, key_grad(w, 0, k), w.start, w.grad_sigma)
+            grads.append(b)
+    else:
+        grads = torch.empty(S, dtype=gdt, device=dev)
+        synth.fill_normal(grads, key_grad_reduced(w, 0), w.start, w.grad_sigma)
+    if w.full_allgather:
+        ag, off = torch.zeros(w.padded, dtype=pdt, device=dev), w.start
+    else:
+        ag, off = torch.zeros(S, dtype=pdt, device=dev), 0
+    q = qs = None
+    if w.quant_block:
+        q = torch.zeros(S, dtype=torch.int8, device=dev)
+        qs = torch.zeros(-(-S // w.quant_block), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+
+    def one():
+        if w.reduce:
+            opt.step_from_rank_buffers(grads, 0, ag, off, op=w.op, q_buf=q, q_scales=qs)
+        else:
+            opt.step_from_reduced(grads, ag, off, q_buf=q, q_scales=qs)
+
     for _ in range(warmup):
-        opt.step_from_rank_buffers(bufs, 0, ag, w.start)
+        one()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        opt.step_from_rank_buffers(bufs, 0, ag, w.start)
+        one()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    del opt, bufs, ag, master
+    st = opt.state.read()
+    assert st.last_skipped == 0, "unexpected skipped step"
+    del opt, grads, ag, master, q, qs
     torch.cuda.empty_cache()
-    return dict(wall=wall)
+    ms = wall / steps * 1e3
+    bpp = step_bytes_per_param(w)
+    return {"ms_per_step": ms, "params_per_s": S / (ms * 1e-3), "bytes_per_param": bpp,
+            "step_GBps": bpp * S / (ms * 1e-3) / 1e9,
+            "step_frac_of_peak": bpp * S / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
 
 def run_copy_calibration(torch, nbytes=4 << 30, reps=3):
@@ -243,15 +295,11 @@ def main():
     if copy:
         out["copy_calibration"] = copy
     if not args.no_variants:
-        w8 = WORKLOADS["10b_n8_reduce8"]
-        r8 = run_reduce8(zf, torch, w8, max(2, args.steps // 2), 1)
-        ms8 = r8["wall"] / max(2, args.steps // 2) * 1e3
-        b8 = (2 * w8.n_ranks + 4 + ADAM_BYTES_PER_PARAM["f32"]) * S
-        out["variants"] = {"10b_n8_reduce8": {
-            "what": "same shard, 8 raw fp16 rank slices reduced (AVG) in the step",
-            "ms_per_step": ms8, "params_per_s": S / (ms8 * 1e-3),
-            "step_GBps": b8 / (ms8 * 1e-3) / 1e9,
-            "step_frac_of_peak": b8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
+        out["variants"] = {}
+        for name, what in VARIANTS:
+            r = run_workload(zf, torch, WORKLOADS[name], max(3, args.steps // 2), 2)
+            r["what"] = what
+            out["variants"][name] = r
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -165,6 +165,8 @@ int zero_grad_reduce_shard(const void* const* grad_bufs, int32_t n_ranks, int32_
     const int es = esize(in_dtype);
     zf::ReduceLaunch a;
     memset(&a, 0, sizeof a);
+    // vector path: each lane reads 4 consecutive inputs (8 B for 16-bit, 16 B
+    // for fp32) and writes 4 fp32 outputs (16 B)
     bool vec = aligned(red_out, 16);
     for (int32_t k = 0; k < n_ranks; ++k) {
         if (!grad_bufs[k]) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: grad_bufs[%d] is NULL", k);
@@ -172,7 +174,7 @@ int zero_grad_reduce_shard(const void* const* grad_bufs, int32_t n_ranks, int32_
             return fail(ZERO_EALIGN, "zero_grad_reduce_shard: grad_bufs[%d] misaligned", k);
         const char* p = static_cast<const char*>(grad_bufs[k]) + elem_offset * es;
         a.bufs[k] = p;
-        vec = vec && aligned(p, 16);
+        vec = vec && aligned(p, 4 * es);
     }
     if (shard_numel == 0) return ok();
     a.n_ranks = n_ranks;
@@ -201,7 +203,7 @@ int zero_unscale_norm(const void* grad_shard, int32_t dtype, int64_t n, zero_ste
     a.n_ranks = 1;
     a.dtype = dtype;
     a.op = ZERO_SUM;
-    a.vec = aligned(grad_shard, 16) ? 1 : 0;
+    a.vec = aligned(grad_shard, 4 * esize(dtype)) ? 1 : 0;
     a.n = n;
     a.red_out = nullptr;
     a.st = d_state;

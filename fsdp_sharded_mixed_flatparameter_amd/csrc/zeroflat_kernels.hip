@@ -15,9 +15,8 @@
 // elements is exactly one INT8 block, reduced across the wave.  All kU
 // slices' loads are issued before any arithmetic (bytes in flight per lane),
 // and every stream uses non-temporal loads/stores: each byte is touched once.
-// By default the grid holds one tile per wave and the hardware dispatcher
-// balances blocks as they retire.  The reduce kernel instead gives each lane 8
-// consecutive elements so its dominant 16-bit reads are 16-byte accesses.
+// By default the AdamW grid holds one tile per wave and the hardware
+// dispatcher balances blocks as they retire.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,7 +45,6 @@ constexpr int kMaxGridReduce = ZERO_MAX_PARTIALS;
 // accesses: every array of the step is touched exactly once per launch.
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f ldnt_f4(const float* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
@@ -63,9 +61,6 @@ __device__ __forceinline__ void stnt_u2(void* p, uint32_t a, uint32_t b) {
     v2u x;
     x.x = a; x.y = b;
     __builtin_nontemporal_store(x, reinterpret_cast<v2u*>(p));
-}
-__device__ __forceinline__ v4u ldnt_u4(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
 }
 __device__ __forceinline__ void stnt_u1(void* p, uint32_t a) {
     __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
@@ -187,144 +182,171 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // red[i] = sum over buffers in rank order (fp32), AVG -> / n_ranks; optional
 // statistics of u = red * (1/loss_scale): per-block fp64 partial of u^2 into
 // st->partials[block] and an overflow flag.  A fold kernel adds the partials
-// into st->sumsq in a fixed order, so the sum is reproducible.
+// into st->sumsq in a fixed order, so the sum is reproducible.  The partials
+// bound the grid (at most ZERO_MAX_PARTIALS blocks), so waves loop over tiles.
 //
-// Mapping: a lane owns 8 consecutive elements of each 512-element chunk (one
-// 16-byte read per 16-bit buffer, 1 KiB per wave instruction); a wave takes
-// TU chunks per iteration so that the one-buffer statistics pass still has
-// TU reads in flight per lane; with many buffers, KC buffers' reads are
-// issued together before they are added (in rank order per element).
-template <int DT, bool VEC, bool WRITE, bool STATS, int TU>
+// Mapping (quad, as the AdamW kernel): in chunk j of a tile, lane l owns
+// elements 256j + 4l .. 4l+3, so every wave instruction covers one contiguous
+// span (512 B of each 16-bit input, 1 KiB of the fp32 output); a lane stride
+// that leaves half of each cache line to another instruction costs about a
+// third of the bandwidth here.
+//
+// Work split: each wave owns one contiguous run of tiles.  Striding the grid
+// over the array instead (every wave in the same narrow window at a time)
+// measured about 20% slower on this part for the 8-buffer reduce.
+//
+// Pipelining: a wave walks (tile, group of KC buffers) pairs in order and
+// issues the reads of the next pair before adding the current one and before
+// storing a finished tile; a scheduling barrier keeps the compiler from sinking
+// them.  KC divides N (chosen by the launcher), so no group is partial and the
+// loop body has no per-buffer branches.
+template <int DT>
+struct RawQuad;
+template <>
+struct RawQuad<ZERO_F32> {
+    v4f x;
+    __device__ __forceinline__ void load(const void* p, int64_t i) {
+        x = ldnt_f4(static_cast<const float*>(p) + i);
+    }
+    __device__ __forceinline__ void add_to(float acc[4]) const {
+        acc[0] = acc[0] + x.x; acc[1] = acc[1] + x.y; acc[2] = acc[2] + x.z; acc[3] = acc[3] + x.w;
+    }
+};
+template <int DT>
+struct RawQuad {
+    v2u w;
+    __device__ __forceinline__ void load(const void* p, int64_t i) {
+        w = ldnt_u2(static_cast<const uint16_t*>(p) + i);
+    }
+    __device__ __forceinline__ void add_to(float acc[4]) const {
+        acc[0] = acc[0] + cvt16<DT>(w.x & 0xffffu);
+        acc[1] = acc[1] + cvt16<DT>(w.x >> 16);
+        acc[2] = acc[2] + cvt16<DT>(w.y & 0xffffu);
+        acc[3] = acc[3] + cvt16<DT>(w.y >> 16);
+    }
+};
+
+template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float inv_n,
                                                           int pow2_n) {
-    constexpr int64_t kT = 512 * TU;
+    constexpr int64_t kT = 256 * TU;
     const int lane = threadIdx.x & 63;
     const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const int64_t n = a.n;
     const int N = a.n_ranks;
+    const int ngroups = N / KC;
     const bool avg = a.op == ZERO_AVG;
     float inv_scale = 1.0f;
     if constexpr (STATS) inv_scale = (float)(1.0 / (double)a.st->loss_scale);
     const float fN = (float)N;
 
-    // Sum of u^2 in two fixed-order binary64 chains (even / odd element of each
-    // pair).  u*u is exact in binary64, so fma(u, u, s) equals s + u*u rounded
-    // once.  No term can overflow binary64 (|u| < 2^128) and squares are >= 0,
-    // so the sum is non-finite exactly when some u is inf or NaN: that is the
-    // overflow test, taken once per lane after the loop.
+    // Sum of u^2 in two fixed-order binary64 chains (elements 0,1 / 2,3 of
+    // each quad).  u*u is exact in binary64, so fma(u, u, s) equals s + u*u
+    // rounded once.  No term can overflow binary64 (|u| < 2^128) and squares
+    // are >= 0, so the sum is non-finite exactly when some u is inf or NaN:
+    // that is the overflow test, taken once per lane after the loop.
     double ss0 = 0.0, ss1 = 0.0;
-    const int64_t ntiles = (n + kT - 1) / kT;
-    const int64_t nfull = VEC ? n / kT : 0;
-    for (int64_t t = wave_id; t < ntiles; t += nwaves) {
-        const int64_t base = t * kT + 8 * lane;
-        float acc[TU][8];
-#pragma unroll
-        for (int j = 0; j < TU; ++j)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[j][c] = 0.0f;
-        const bool full = t < nfull;
-        if (full) {
-            if constexpr (DT == ZERO_F32) {
-                for (int k = 0; k < N; ++k) {
-                    const float* b = static_cast<const float*>(a.bufs[k]) + base;
-                    v4f x[TU][2];
-#pragma unroll
-                    for (int j = 0; j < TU; ++j) {
-                        x[j][0] = ldnt_f4(b + 512 * j);
-                        x[j][1] = ldnt_f4(b + 512 * j + 4);
-                    }
-#pragma unroll
-                    for (int j = 0; j < TU; ++j) {
-                        acc[j][0] = acc[j][0] + x[j][0].x; acc[j][1] = acc[j][1] + x[j][0].y;
-                        acc[j][2] = acc[j][2] + x[j][0].z; acc[j][3] = acc[j][3] + x[j][0].w;
-                        acc[j][4] = acc[j][4] + x[j][1].x; acc[j][5] = acc[j][5] + x[j][1].y;
-                        acc[j][6] = acc[j][6] + x[j][1].z; acc[j][7] = acc[j][7] + x[j][1].w;
-                    }
-                }
-            } else {
-                constexpr int KC = TU >= 4 ? 1 : 8 / TU;  // buffers whose reads issue together
-                int k = 0;
-                for (; k + KC <= N; k += KC) {
-                    v4u w[KC][TU];
-#pragma unroll
-                    for (int kk = 0; kk < KC; ++kk)
-#pragma unroll
-                        for (int j = 0; j < TU; ++j)
-                            w[kk][j] = ldnt_u4(static_cast<const uint16_t*>(a.bufs[k + kk]) +
-                                               base + 512 * j);
-#pragma unroll
-                    for (int kk = 0; kk < KC; ++kk) {  // rank order per element
-#pragma unroll
-                        for (int j = 0; j < TU; ++j) {
-                            acc[j][0] = acc[j][0] + cvt16<DT>(w[kk][j].x & 0xffffu);
-                            acc[j][1] = acc[j][1] + cvt16<DT>(w[kk][j].x >> 16);
-                            acc[j][2] = acc[j][2] + cvt16<DT>(w[kk][j].y & 0xffffu);
-                            acc[j][3] = acc[j][3] + cvt16<DT>(w[kk][j].y >> 16);
-                            acc[j][4] = acc[j][4] + cvt16<DT>(w[kk][j].z & 0xffffu);
-                            acc[j][5] = acc[j][5] + cvt16<DT>(w[kk][j].z >> 16);
-                            acc[j][6] = acc[j][6] + cvt16<DT>(w[kk][j].w & 0xffffu);
-                            acc[j][7] = acc[j][7] + cvt16<DT>(w[kk][j].w >> 16);
-                        }
-                    }
-                }
-                for (; k < N; ++k) {
-                    v4u w[TU];
-#pragma unroll
-                    for (int j = 0; j < TU; ++j)
-                        w[j] = ldnt_u4(static_cast<const uint16_t*>(a.bufs[k]) + base + 512 * j);
-#pragma unroll
-                    for (int j = 0; j < TU; ++j) {
-                        acc[j][0] = acc[j][0] + cvt16<DT>(w[j].x & 0xffffu);
-                        acc[j][1] = acc[j][1] + cvt16<DT>(w[j].x >> 16);
-                        acc[j][2] = acc[j][2] + cvt16<DT>(w[j].y & 0xffffu);
-                        acc[j][3] = acc[j][3] + cvt16<DT>(w[j].y >> 16);
-                        acc[j][4] = acc[j][4] + cvt16<DT>(w[j].z & 0xffffu);
-                        acc[j][5] = acc[j][5] + cvt16<DT>(w[j].z >> 16);
-                        acc[j][6] = acc[j][6] + cvt16<DT>(w[j].w & 0xffffu);
-                        acc[j][7] = acc[j][7] + cvt16<DT>(w[j].w >> 16);
-                    }
-                }
-            }
-        } else {
-            for (int k = 0; k < N; ++k) {
-#pragma unroll
-                for (int j = 0; j < TU; ++j)
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        const int64_t i = base + 512 * j + c;
-                        if (i < n) acc[j][c] = acc[j][c] + load_one<DT>(a.bufs[k], i);
-                    }
-            }
-        }
+
+    auto finish = [&](const float (&acc)[TU][4], int64_t base, bool full) {
 #pragma unroll
         for (int j = 0; j < TU; ++j) {
-            const int64_t i0 = base + 512 * j;
-            float red[8];
+            const int64_t i0 = base + 256 * j;
+            float red[4];
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                red[c] = !avg ? acc[j][c] : (pow2_n ? acc[j][c] * inv_n : acc[j][c] / fN);
+            for (int c = 0; c < 4; ++c) {
+                const float q = pow2_n ? acc[j][c] * inv_n : acc[j][c] / fN;
+                red[c] = avg ? q : acc[j][c];
+            }
             if constexpr (WRITE) {
                 if (full) {
                     stnt_f4(a.red_out + i0, red[0], red[1], red[2], red[3]);
-                    stnt_f4(a.red_out + i0 + 4, red[4], red[5], red[6], red[7]);
                 } else {
 #pragma unroll
-                    for (int c = 0; c < 8; ++c)
+                    for (int c = 0; c < 4; ++c)
                         if (i0 + c < n) a.red_out[i0 + c] = red[c];
                 }
             }
             if constexpr (STATS) {
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
+                for (int c = 0; c < 4; ++c) {
                     if (full || i0 + c < n) {
                         const double u = (double)(red[c] * inv_scale);
-                        if (c & 1) ss1 = __builtin_fma(u, u, ss1);
+                        if (c & 2) ss1 = __builtin_fma(u, u, ss1);
                         else ss0 = __builtin_fma(u, u, ss0);
                     }
                 }
             }
         }
+    };
+
+    const int64_t ntiles = (n + kT - 1) / kT;
+    const int64_t nfull = VEC ? n / kT : 0;
+    // ---- full tiles: wave w owns tiles [w*per, min((w+1)*per, nfull))
+    const int64_t per = (nfull + nwaves - 1) / nwaves;
+    const int64_t t_begin = wave_id * per;
+    const int64_t t_end = t_begin + per < nfull ? t_begin + per : nfull;
+    if (t_begin < t_end) {
+        RawQuad<DT> cur[KC][TU], nxt[KC][TU];
+        auto load_group = [&](RawQuad<DT> (&x)[KC][TU], int64_t tt, int gg) {
+            const int64_t base = tt * kT + 4 * lane;
+#pragma unroll
+            for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+                for (int j = 0; j < TU; ++j) x[kk][j].load(a.bufs[gg * KC + kk], base + 256 * j);
+        };
+        load_group(cur, t_begin, 0);
+        int64_t t = t_begin;
+        int g = 0;
+        float acc[TU][4];
+#pragma unroll
+        for (int j = 0; j < TU; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[j][c] = 0.0f;
+        for (;;) {
+            // the pair after (t, g); past the run's end it re-reads the last
+            // pair (harmless, in bounds, never used)
+            int gn = g + 1;
+            int64_t tn = t;
+            if (gn == ngroups) { gn = 0; tn = t + 1; }
+            const bool more = tn < t_end;
+            load_group(nxt, more ? tn : t, more ? gn : g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < KC; ++kk)                  // rank order per element
+#pragma unroll
+                for (int j = 0; j < TU; ++j) cur[kk][j].add_to(acc[j]);
+            if (gn == 0) {                                   // tile t complete
+                finish(acc, t * kT + 4 * lane, true);
+#pragma unroll
+                for (int j = 0; j < TU; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[j][c] = 0.0f;
+            }
+            if (!more) break;
+            __builtin_memcpy(cur, nxt, sizeof(cur));         // register renaming
+            t = tn;
+            g = gn;
+        }
+    }
+    // ---- the ragged tail (or every tile, without the vector path): element-wise
+    for (int64_t t = nfull + wave_id; t < ntiles; t += nwaves) {
+        const int64_t base = t * kT + 4 * lane;
+        float acc[TU][4];
+#pragma unroll
+        for (int j = 0; j < TU; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[j][c] = 0.0f;
+        for (int k = 0; k < N; ++k) {
+#pragma unroll
+            for (int j = 0; j < TU; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t i = base + 256 * j + c;
+                    if (i < n) acc[j][c] = acc[j][c] + load_one<DT>(a.bufs[k], i);
+                }
+        }
+        finish(acc, base, false);
     }
     if constexpr (STATS) {
         const double mine = ss0 + ss1;
@@ -541,22 +563,46 @@ int grid_for_tiles(int64_t ntiles, int cap) {
     return (int)g;
 }
 
+// Blocks of `kernel` resident at once on the current device (CUs x blocks
+// per CU at the kernel's register occupancy), cached per device.
+template <typename K>
+int resident_blocks(K kernel) {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] > 0) return cache[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
+        return 0;
+    cache[dev] = cus * per_cu;
+    return cache[dev];
+}
+
+// The reduce grid is persistent (one partial sum per block, at most
+// ZERO_MAX_PARTIALS blocks): a whole number of resident rounds, so that no
+// partly filled last round leaves the machine idle while it drains.
+template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC>
+void launch_reduce_shape(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
+    auto kernel = reduce_kernel<DT, VEC, WRITE, STATS, TU, KC>;
+    const int64_t ntiles = (a.n + 256 * TU - 1) / (256 * TU);
+    int grid = grid_for_tiles(ntiles, kMaxGridReduce);
+    const int round = resident_blocks(kernel);
+    if (round > 0 && grid > round) grid = (grid / round) * round;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, a, inv_n,
+                       pow2);
+}
+
 template <int DT, bool VEC, bool WRITE, bool STATS>
 int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     const int N = a.n_ranks;
     const int pow2 = (N & (N - 1)) == 0;
     const float inv_n = 1.0f / (float)N;  // exact when N is a power of two
-    if (N <= 2) {   // few buffers: 4 chunks per lane keep reads in flight
-        const int64_t ntiles = (a.n + 2048 - 1) / 2048;
-        const int grid = grid_for_tiles(ntiles, kMaxGridReduce);
-        hipLaunchKernelGGL((reduce_kernel<DT, VEC, WRITE, STATS, 4>), dim3(grid), dim3(kThreads),
-                           0, (hipStream_t)stream, a, inv_n, pow2);
-    } else {
-        const int64_t ntiles = (a.n + 512 - 1) / 512;
-        const int grid = grid_for_tiles(ntiles, kMaxGridReduce);
-        hipLaunchKernelGGL((reduce_kernel<DT, VEC, WRITE, STATS, 1>), dim3(grid), dim3(kThreads),
-                           0, (hipStream_t)stream, a, inv_n, pow2);
-    }
+    // reads in flight per lane: TU chunks x KC buffers (KC divides N)
+    if (N % 8 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 8>(a, stream, inv_n, pow2);
+    else if (N % 4 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 4>(a, stream, inv_n, pow2);
+    else if (N % 2 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 4, 2>(a, stream, inv_n, pow2);
+    else launch_reduce_shape<DT, VEC, WRITE, STATS, 8, 1>(a, stream, inv_n, pow2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (STATS) {
