@@ -206,6 +206,27 @@ void oracle_reduce(const void* const* bufs, int32_t n_ranks, int32_t dtype, int6
 }
 
 /* ------------------------------------------------------------------------ */
+/* Gradient accumulation in the sharded state.                               */
+/* [DS] "实践要点" (gradient accumulation): a large batch is split into      */
+/* micro-batches whose gradients are summed before one optimizer step, the  */
+/* loss being divided by the number of micro-steps; [RD] §5.3: under ZeRO   */
+/* the gradients are accumulated while sharded; [RD] §5.1 configures two    */
+/* accumulation steps.  Reading: every micro-step reduces its N rank        */
+/* buffers exactly as oracle_reduce does (the Reduce-Scatter output of that */
+/* micro-step), then adds that result to the rank's fp32 shard:             */
+/*   acc[i] = acc[i] + red_i.  The 1/steps factor is already in the         */
+/* gradients (it is applied to the loss before backward).                   */
+/* ------------------------------------------------------------------------ */
+void oracle_reduce_accumulate(const void* const* bufs, int32_t n_ranks, int32_t dtype,
+                              int64_t offset, int64_t n, int32_t op, float* acc) {
+    for (int64_t i = 0; i < n; ++i) {
+        float red;
+        oracle_reduce(bufs, n_ranks, dtype, offset + i, 1, op, &red);
+        acc[i] = acc[i] + red;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Unscale, overflow test, local sum of squares.                             */
 /* [RD] §5.1 (fp16 loss scaling, initial scale 2^16) and §5.3 (overflow is  */
 /* detected on the gradients; clipping uses the global gradient norm).      */
@@ -304,6 +325,32 @@ void oracle_quant_int8(const void* x, int32_t dtype, int64_t n, int32_t block, i
             if (r > 127.0f) r = 127.0f;
             if (r < -127.0f) r = -127.0f;
             q[j] = (int8_t)r;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT8 All-Gather consumer.                                                 */
+/* [DS] "ZeRO++：量化通信压缩": the receiver dequantises the int8/int4       */
+/* parameter shards it gathers; [RD] §4.2: the INT8 weights are restored    */
+/* only just before local compute; [DS] "FSDP 的分片粒度与 FlatParameter":  */
+/* the gathered flat buffer is then unflattened into the parameters (views  */
+/* at each parameter's [start, end) flat range, no arithmetic).             */
+/* The gathered payload holds n_slots rank slots: slot s's codes at         */
+/* q[s*S .. s*S+S) and its scales at scales[s*nb ..), nb = ceil(S/block),   */
+/* blocks restarting at each slot's start (as the producer wrote them).     */
+/* Reading: x = f32(q) * scale, one binary32 product, then rounded to the   */
+/* parameter format (RNE); out[s*S + i] in the full flat buffer.            */
+/* ------------------------------------------------------------------------ */
+void oracle_dequant_int8(const int8_t* q, const float* scales, int32_t n_slots,
+                         int64_t slot_numel, int32_t block, int32_t dtype, void* out) {
+    const int64_t nb = (slot_numel + block - 1) / block;
+    for (int32_t s = 0; s < n_slots; ++s) {
+        for (int64_t i = 0; i < slot_numel; ++i) {
+            const int64_t j = (int64_t)s * slot_numel + i;
+            const float x = (float)q[j] * scales[(int64_t)s * nb + i / block];
+            if (dtype == OR_F32) static_cast<float*>(out)[j] = x;
+            else store_lp(out, dtype, j, x);
         }
     }
 }

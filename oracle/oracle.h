@@ -72,6 +72,11 @@ void oracle_accounting(int64_t total, int64_t shard, int32_t param_bytes,
 void oracle_reduce(const void* const* bufs, int32_t n_ranks, int32_t dtype,
                    int64_t offset, int64_t n, int32_t op, float* red);
 
+/* Gradient accumulation in the sharded state: acc[i] = acc[i] + red_i, with
+ * red_i exactly oracle_reduce's value for this micro-step's buffers. */
+void oracle_reduce_accumulate(const void* const* bufs, int32_t n_ranks, int32_t dtype,
+                              int64_t offset, int64_t n, int32_t op, float* acc);
+
 /* Unscale + overflow + local sum of squares over g[0..n):
  *   u_i = f32(g_i) * f32(1/loss_scale); overflow |= !isfinite(u_i);
  *   sumsq += (double)u_i * (double)u_i, in index order. */
@@ -98,6 +103,12 @@ void oracle_adamw(const void* g, int32_t gdtype, float* p, float* m, float* v, i
  * elements (the last may be short) scale = amax/127, q = clamp(rint(x/scale)). */
 void oracle_quant_int8(const void* x, int32_t dtype, int64_t n, int32_t block,
                        int8_t* q, float* scales);
+
+/* INT8 All-Gather consumer: n_slots slots of slot_numel codes (scales of
+ * slot s at s*ceil(slot_numel/block)) -> out[s*slot_numel + i] =
+ * round_dtype(f32(q) * scale); dtype OR_F32, OR_F16 or OR_BF16. */
+void oracle_dequant_int8(const int8_t* q, const float* scales, int32_t n_slots,
+                         int64_t slot_numel, int32_t block, int32_t dtype, void* out);
 
 /* Dynamic/static loss scaler, applied once per step after the overflow test. */
 typedef struct {

@@ -90,6 +90,12 @@ def lib():
         L.oracle_quant_int8.restype = None
         L.oracle_quant_int8.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int32,
                                         C.c_void_p, C.c_void_p]
+        L.oracle_reduce_accumulate.restype = None
+        L.oracle_reduce_accumulate.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int64,
+                                               C.c_int64, C.c_int32, C.c_void_p]
+        L.oracle_dequant_int8.restype = None
+        L.oracle_dequant_int8.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64,
+                                          C.c_int32, C.c_int32, C.c_void_p]
         L.oracle_scaler_update.restype = None
         L.oracle_scaler_update.argtypes = [C.POINTER(Scaler), C.c_int32]
         _lib = L
@@ -186,6 +192,18 @@ def reduce(bufs, dtype, offset, n, op):
     return red
 
 
+def reduce_accumulate(bufs, dtype, offset, n, op, acc):
+    """acc[i] += red_i (one micro-step of sharded gradient accumulation), in place."""
+    for b in bufs:
+        _check(b, dtype_np(dtype))
+        assert offset + n <= b.size
+    _check(acc, np.float32)
+    assert acc.size >= n
+    arr = (C.c_void_p * len(bufs))(*[b.ctypes.data for b in bufs])
+    lib().oracle_reduce_accumulate(arr, len(bufs), dtype, offset, n, op, _ptr(acc))
+    return acc
+
+
 def unscale_stats(g, dtype, loss_scale, sumsq=0.0, overflow=0):
     _check(g, dtype_np(dtype))
     s = C.c_double(sumsq)
@@ -221,6 +239,18 @@ def quant_int8(x, dtype, block=256):
     s = np.empty(nb, np.float32)
     lib().oracle_quant_int8(_ptr(x), dtype, x.size, block, _ptr(q), _ptr(s))
     return q, s
+
+
+def dequant_int8(q, scales, n_slots, slot_numel, block, dtype):
+    """Full flat buffer out[s*S+i] = round_dtype(f32(q) * scale) over n_slots slots;
+    uint16 bit patterns for fp16/bf16, float32 for F32."""
+    _check(q, np.int8)
+    _check(scales, np.float32)
+    nb = (slot_numel + block - 1) // block
+    assert q.size >= n_slots * slot_numel and scales.size >= n_slots * nb
+    out = np.empty(n_slots * slot_numel, np.float32 if dtype == F32 else np.uint16)
+    lib().oracle_dequant_int8(_ptr(q), _ptr(scales), n_slots, slot_numel, block, dtype, _ptr(out))
+    return out
 
 
 def scaler_update(sc, overflow):

@@ -16,6 +16,7 @@ SRC = os.path.join(ROOT, "oracle", "oracle.cpp")
 STEP = "tests/test_oracle_step.py"
 FMT = "tests/test_oracle_formats.py"
 LAY = "tests/test_oracle_layout.py"
+CONS = "tests/test_oracle_consumer.py"
 
 # (name, original text, planted mistake, tests expected to fail)
 MUTANTS = [
@@ -84,6 +85,28 @@ MUTANTS = [
     ("acct_z1_optim_replicated",
      "out[1] = (int64_t)P * total + (int64_t)G * total + (int64_t)K * shard;",
      "out[1] = (int64_t)P * total + (int64_t)G * total + (int64_t)K * total;", LAY),
+    ("dequant_global_block_index", "scales[(int64_t)s * nb + i / block]", "scales[j / block]",
+     CONS),
+    ("dequant_slot_not_offset", "const int64_t j = (int64_t)s * slot_numel + i;",
+     "const int64_t j = i;", CONS),
+    ("dequant_divides", "const float x = (float)q[j] * scales[", "const float x = (float)q[j] / scales[",
+     CONS),
+    ("dequant_code_as_unsigned", "const float x = (float)q[j] * scales[",
+     "const float x = (float)(uint8_t)q[j] * scales[", CONS),
+    ("dequant_bf16_truncates", "if (dtype == OR_F32) static_cast<float*>(out)[j] = x;\n"
+     "            else store_lp(out, dtype, j, x);",
+     "if (dtype == OR_F32) static_cast<float*>(out)[j] = x;\n"
+     "            else if (dtype == OR_BF16) static_cast<uint16_t*>(out)[j] = "
+     "(uint16_t)(f32_bits(x) >> 16);\n            else store_lp(out, dtype, j, x);", CONS),
+    ("accumulate_overwrites", "acc[i] = acc[i] + red;", "acc[i] = red;", CONS),
+    ("accumulate_rank_by_rank",
+     "        float red;\n        oracle_reduce(bufs, n_ranks, dtype, offset + i, 1, op, &red);\n"
+     "        acc[i] = acc[i] + red;",
+     "        for (int32_t k = 0; k < n_ranks; ++k) acc[i] = acc[i] + load_elem(bufs[k], dtype, "
+     "offset + i);", CONS),
+    ("accumulate_avg_ignored",
+     "oracle_reduce(bufs, n_ranks, dtype, offset + i, 1, op, &red);",
+     "oracle_reduce(bufs, n_ranks, dtype, offset + i, 1, OR_SUM, &red);", CONS),
 ]
 
 
