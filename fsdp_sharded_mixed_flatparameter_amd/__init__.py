@@ -22,7 +22,7 @@ ZERO_MAX_PARTIALS = 2048
 
 EXPORTS = ("zero_last_error", "zero_flat_layout", "zero_step_state_init",
            "zero_grad_reduce_shard", "zero_unscale_norm", "zero_adamw_shard_step",
-           "zero_quant_allgather_slot")
+           "zero_quant_allgather_slot", "zero_dequant_allgather", "zero_grad_accumulate_shard")
 
 
 class zero_span_t(C.Structure):
@@ -78,6 +78,10 @@ def _load():
                                         i64, i32, vp, u32, vp, vp]
     L.zero_quant_allgather_slot.restype = C.c_int
     L.zero_quant_allgather_slot.argtypes = [vp, i32, i64, i32, vp, i64, vp, i64, vp]
+    L.zero_dequant_allgather.restype = C.c_int
+    L.zero_dequant_allgather.argtypes = [vp, vp, i32, i64, i32, vp, i32, vp]
+    L.zero_grad_accumulate_shard.restype = C.c_int
+    L.zero_grad_accumulate_shard.argtypes = [vp, i32, i32, i64, i64, i32, vp, vp, vp]
     return L
 
 
@@ -194,10 +198,7 @@ def _state_ptr(state):
 
 
 # ------------------------------------------------------------------ the step
-def zero_grad_reduce_shard(grad_bufs, elem_offset, shard_numel, op, red_out, state=None,
-                           stream=None):
-    """red_out[i] = sum_k grad_bufs[k][elem_offset + i] (rank order), AVG -> / N;
-    accumulates the step statistics into `state` when given."""
+def _rank_buffers(grad_bufs, elem_offset, shard_numel, out):
     if not grad_bufs:
         raise ValueError("grad_bufs is empty")
     dt = _dtype_code(grad_bufs[0])
@@ -207,12 +208,29 @@ def zero_grad_reduce_shard(grad_bufs, elem_offset, shard_numel, op, red_out, sta
             raise ValueError("grad_bufs dtypes differ")
         if elem_offset + shard_numel > b.numel():
             raise ValueError("grad_bufs[%d] is shorter than elem_offset + shard_numel" % k)
-    _contig(red_out, "red_out")
-    if red_out.dtype.itemsize != 4 or red_out.numel() < shard_numel:
-        raise ValueError("red_out must be float32 with >= shard_numel elements")
-    arr = (C.c_void_p * len(grad_bufs))(*[b.data_ptr() for b in grad_bufs])
+    _contig(out, "output shard")
+    if _dtype_code(out) != ZERO_F32 or out.numel() < shard_numel:
+        raise ValueError("the output shard must be float32 with >= shard_numel elements")
+    return dt, (C.c_void_p * len(grad_bufs))(*[b.data_ptr() for b in grad_bufs])
+
+
+def zero_grad_reduce_shard(grad_bufs, elem_offset, shard_numel, op, red_out, state=None,
+                           stream=None):
+    """red_out[i] = sum_k grad_bufs[k][elem_offset + i] (rank order), AVG -> / N;
+    accumulates the step statistics into `state` when given."""
+    dt, arr = _rank_buffers(grad_bufs, elem_offset, shard_numel, red_out)
     _check(_lib.zero_grad_reduce_shard(arr, len(grad_bufs), dt, elem_offset, shard_numel, op,
                                        _ptr(red_out), _state_ptr(state), _stream(stream)))
+
+
+def zero_grad_accumulate_shard(grad_bufs, elem_offset, shard_numel, op, acc, state=None,
+                               stream=None):
+    """One micro-step of sharded gradient accumulation: acc[i] += the reduce of
+    grad_bufs over [elem_offset, +shard_numel); pass `state` on the last
+    micro-step to take the step statistics over the accumulated shard."""
+    dt, arr = _rank_buffers(grad_bufs, elem_offset, shard_numel, acc)
+    _check(_lib.zero_grad_accumulate_shard(arr, len(grad_bufs), dt, elem_offset, shard_numel,
+                                           op, _ptr(acc), _state_ptr(state), _stream(stream)))
 
 
 def zero_unscale_norm(grad_shard, state, n=None, stream=None):
@@ -256,6 +274,36 @@ def zero_quant_allgather_slot(slot, q_buf, q_scales, q_slot_offset=0, q_scale_of
     _check(_lib.zero_quant_allgather_slot(_ptr(slot), _dtype_code(slot), n, block, _ptr(q_buf),
                                           q_slot_offset, _ptr(q_scales), q_scale_offset,
                                           _stream(stream)))
+
+
+
+
+# ------------------------------------------------------------------ All-Gather consumer
+def zero_dequant_allgather(q_buf, q_scales, n_slots, slot_numel, out, block=256, stream=None):
+    """out[s*S + i] = round(f32(q) * scale) over the n_slots gathered INT8 slots
+    (the full flat parameter, fp16/bf16 or fp32)."""
+    for name, t in (("q_buf", q_buf), ("q_scales", q_scales), ("out", out)):
+        _contig(t, name)
+    import torch
+    if q_buf.dtype != torch.int8 or q_scales.dtype != torch.float32:
+        raise ValueError("q_buf must be int8 and q_scales float32")
+    nb = (slot_numel + block - 1) // block
+    if q_buf.numel() < n_slots * slot_numel or q_scales.numel() < n_slots * nb or \
+            out.numel() < n_slots * slot_numel:
+        raise ValueError("buffers are shorter than n_slots slots")
+    _check(_lib.zero_dequant_allgather(_ptr(q_buf), _ptr(q_scales), n_slots, slot_numel, block,
+                                       _ptr(out), _dtype_code(out), _stream(stream)))
+
+
+def unflatten(flat, shapes, n_ranks=1, align=1):
+    """Views of the parameters inside a gathered flat buffer, at the [start, end)
+    ranges zero_flat_layout gives for these shapes (no copy)."""
+    import math
+    numels = [int(math.prod(sh)) for sh in shapes]
+    lay = zero_flat_layout(numels, n_ranks, align)
+    if flat.numel() < lay["total"]:
+        raise ValueError("flat buffer is shorter than the parameters")
+    return [flat[a:b].view(tuple(sh)) for (a, b), sh in zip(lay["spans"], shapes)]
 
 
 from . import shard  # noqa: E402

@@ -149,29 +149,32 @@ int zero_step_state_init(zero_step_state_t* st, float loss_scale, int32_t dynami
 }
 
 // ---------------------------------------------------------------------------
-int zero_grad_reduce_shard(const void* const* grad_bufs, int32_t n_ranks, int32_t in_dtype,
-                           int64_t elem_offset, int64_t shard_numel, int32_t op,
-                           float* red_out, zero_step_state_t* d_state, void* stream) {
-    if (!grad_bufs) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: grad_bufs is NULL");
+namespace {
+// zero_grad_reduce_shard and zero_grad_accumulate_shard: the same reduce, the
+// second adding into its output instead of overwriting it.
+int reduce_entry(const char* fn, const void* const* grad_bufs, int32_t n_ranks, int32_t in_dtype,
+                 int64_t elem_offset, int64_t shard_numel, int32_t op, float* red_out,
+                 int accumulate, zero_step_state_t* d_state, void* stream) {
+    if (!grad_bufs) return fail(ZERO_EINVAL, "%s: grad_bufs is NULL", fn);
     if (n_ranks < 1 || n_ranks > ZERO_MAX_RANKS)
-        return fail(ZERO_ERANGE, "zero_grad_reduce_shard: n_ranks %d not in [1, %d]", n_ranks, ZERO_MAX_RANKS);
-    if (!valid_dtype(in_dtype)) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: bad in_dtype %d", in_dtype);
-    if (op != ZERO_SUM && op != ZERO_AVG) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: bad op %d", op);
+        return fail(ZERO_ERANGE, "%s: n_ranks %d not in [1, %d]", fn, n_ranks, ZERO_MAX_RANKS);
+    if (!valid_dtype(in_dtype)) return fail(ZERO_EINVAL, "%s: bad in_dtype %d", fn, in_dtype);
+    if (op != ZERO_SUM && op != ZERO_AVG) return fail(ZERO_EINVAL, "%s: bad op %d", fn, op);
     if (elem_offset < 0 || shard_numel < 0)
-        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: negative offset or size");
-    if (!red_out) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: red_out is NULL");
-    if (!aligned(red_out, 4)) return fail(ZERO_EALIGN, "zero_grad_reduce_shard: red_out not 4-byte aligned");
-    if (d_state && !aligned(d_state, 8)) return fail(ZERO_EALIGN, "zero_grad_reduce_shard: state not 8-byte aligned");
+        return fail(ZERO_EINVAL, "%s: negative offset or size", fn);
+    if (!red_out) return fail(ZERO_EINVAL, "%s: output shard is NULL", fn);
+    if (!aligned(red_out, 4)) return fail(ZERO_EALIGN, "%s: output shard not 4-byte aligned", fn);
+    if (d_state && !aligned(d_state, 8)) return fail(ZERO_EALIGN, "%s: state not 8-byte aligned", fn);
     const int es = esize(in_dtype);
     zf::ReduceLaunch a;
     memset(&a, 0, sizeof a);
     // vector path: each lane reads 4 consecutive inputs (8 B for 16-bit, 16 B
-    // for fp32) and writes 4 fp32 outputs (16 B)
+    // for fp32) and writes (and, accumulating, reads) 4 fp32 outputs (16 B)
     bool vec = aligned(red_out, 16);
     for (int32_t k = 0; k < n_ranks; ++k) {
-        if (!grad_bufs[k]) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: grad_bufs[%d] is NULL", k);
+        if (!grad_bufs[k]) return fail(ZERO_EINVAL, "%s: grad_bufs[%d] is NULL", fn, k);
         if (!aligned(grad_bufs[k], es))
-            return fail(ZERO_EALIGN, "zero_grad_reduce_shard: grad_bufs[%d] misaligned", k);
+            return fail(ZERO_EALIGN, "%s: grad_bufs[%d] misaligned", fn, k);
         const char* p = static_cast<const char*>(grad_bufs[k]) + elem_offset * es;
         a.bufs[k] = p;
         vec = vec && aligned(p, 4 * es);
@@ -183,10 +186,29 @@ int zero_grad_reduce_shard(const void* const* grad_bufs, int32_t n_ranks, int32_
     a.vec = vec ? 1 : 0;
     a.n = shard_numel;
     a.red_out = red_out;
+    a.accumulate = accumulate;
     a.st = d_state;
     const int e = zf::launch_reduce_stats(a, stream);
-    if (e) return hip_fail(e, "zero_grad_reduce_shard");
+    if (e) return hip_fail(e, fn);
     return ok();
+}
+}  // namespace
+
+int zero_grad_reduce_shard(const void* const* grad_bufs, int32_t n_ranks, int32_t in_dtype,
+                           int64_t elem_offset, int64_t shard_numel, int32_t op,
+                           float* red_out, zero_step_state_t* d_state, void* stream) {
+    return reduce_entry("zero_grad_reduce_shard", grad_bufs, n_ranks, in_dtype, elem_offset,
+                        shard_numel, op, red_out, 0, d_state, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Gradient accumulation in the sharded state ("DeepSpeed 与 FSDP", 实践要点;
+// 2kiu.com §5.3): acc += this micro-step's reduce.
+int zero_grad_accumulate_shard(const void* const* grad_bufs, int32_t n_ranks, int32_t in_dtype,
+                               int64_t elem_offset, int64_t shard_numel, int32_t op, float* acc,
+                               zero_step_state_t* d_state, void* stream) {
+    return reduce_entry("zero_grad_accumulate_shard", grad_bufs, n_ranks, in_dtype, elem_offset,
+                        shard_numel, op, acc, 1, d_state, stream);
 }
 
 int zero_unscale_norm(const void* grad_shard, int32_t dtype, int64_t n, zero_step_state_t* d_state,
@@ -300,6 +322,41 @@ int zero_quant_allgather_slot(const void* slot, int32_t dtype, int64_t n, int32_
     a.qs = q_scales + q_scale_offset;
     a.vec = (aligned(slot, 8) && aligned(a.q, 4)) ? 1 : 0;
     const int e = zf::launch_quant(a, stream);
+    if (e) return hip_fail(e, fn);
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// INT8 All-Gather consumer ("DeepSpeed 与 FSDP", ZeRO++：量化通信压缩;
+// 2kiu.com §4.2): the gathered slots back to the flat parameter.
+int zero_dequant_allgather(const int8_t* q_buf, const float* q_scales, int32_t n_slots,
+                           int64_t slot_numel, int32_t block, void* out, int32_t out_dtype,
+                           void* stream) {
+    const char* fn = "zero_dequant_allgather";
+    if (!valid_dtype(out_dtype)) return fail(ZERO_EINVAL, "%s: bad out_dtype %d", fn, out_dtype);
+    if (n_slots < 1 || n_slots > 65536) return fail(ZERO_ERANGE, "%s: n_slots %d not in [1, 65536]", fn, n_slots);
+    if (slot_numel < 0) return fail(ZERO_EINVAL, "%s: negative slot_numel", fn);
+    if (block < 4 || block % 4 != 0) return fail(ZERO_EINVAL, "%s: block %d is not a positive multiple of 4", fn, block);
+    int64_t total = 0;
+    if (!mul_ok(slot_numel, n_slots, &total) || !mul_ok(total, 4, &total))
+        return fail(ZERO_ERANGE, "%s: n_slots * slot_numel overflows", fn);
+    if (slot_numel == 0) return ok();
+    if (!q_buf || !q_scales || !out) return fail(ZERO_EINVAL, "%s: NULL pointer", fn);
+    const int es = esize(out_dtype);
+    if (!aligned(q_scales, 4) || !aligned(out, es)) return fail(ZERO_EALIGN, "%s: misaligned", fn);
+    zf::DequantLaunch a;
+    memset(&a, 0, sizeof a);
+    a.q = q_buf;
+    a.qs = q_scales;
+    a.out = out;
+    a.out_dtype = out_dtype;
+    a.block = block;
+    a.n_slots = n_slots;
+    a.slot_numel = slot_numel;
+    // quad path: 4 codes (4 B) in, 4 outputs (8 B 16-bit, 16 B fp32) out per
+    // lane; slot starts keep the alignment when slot_numel % 4 == 0
+    a.vec = (slot_numel % 4 == 0 && aligned(q_buf, 4) && aligned(out, 4 * es)) ? 1 : 0;
+    const int e = zf::launch_dequant(a, stream);
     if (e) return hip_fail(e, fn);
     return ok();
 }

@@ -38,7 +38,10 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kU = ZF_ADAM_U;               // 256-element slices per adamw/quant tile
 constexpr int64_t kTile = 256 * kU;         // adamw/quant tile (elements per wave)
-constexpr int kMaxGridStep = ZF_ADAM_GRID > 0 ? ZF_ADAM_GRID : 0x7fffffff;
+// Streaming kernels loop over tiles when the grid is capped; 2^22 blocks of
+// 256 threads keep every launch inside HIP's 2^32-thread grid limit.
+constexpr int kMaxGridStream = 1 << 22;
+constexpr int kMaxGridStep = ZF_ADAM_GRID > 0 ? ZF_ADAM_GRID : kMaxGridStream;
 constexpr int kMaxGridReduce = ZERO_MAX_PARTIALS;
 
 // Native vectors for the non-temporal (streaming, read-once / write-once)
@@ -124,6 +127,15 @@ __device__ __forceinline__ void load_quad(const void* p, int64_t i, float out[4]
         out[2] = cvt16<DT>(w.y & 0xffffu);
         out[3] = cvt16<DT>(w.y >> 16);
     }
+}
+
+// This wave's index in the grid, made a scalar (wave-uniform) value: loop
+// bounds and tile indices derived from it then live in SGPRs, so per-tile
+// pointers (the rank-buffer table in the kernel arguments) are fetched with
+// scalar loads, which do not wait in the vector-memory counter behind the
+// streaming loads in flight.
+__device__ __forceinline__ int64_t wave_index() {
+    return (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
 // ---------------------------------------------------------------- reductions
@@ -226,12 +238,13 @@ struct RawQuad {
     }
 };
 
-template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC>
+template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float inv_n,
                                                           int pow2_n) {
+    static_assert(WRITE || !ACC, "accumulation writes its output");
     constexpr int64_t kT = 256 * TU;
     const int lane = threadIdx.x & 63;
-    const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t wave_id = wave_index();
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const int64_t n = a.n;
     const int N = a.n_ranks;
@@ -248,7 +261,9 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
     // that is the overflow test, taken once per lane after the loop.
     double ss0 = 0.0, ss1 = 0.0;
 
-    auto finish = [&](const float (&acc)[TU][4], int64_t base, bool full) {
+    // prev: the shard's accumulated values for these elements (ACC only)
+    auto finish = [&](const float (&acc)[TU][4], const float (&prev)[TU][4], int64_t base,
+                      bool full) {
 #pragma unroll
         for (int j = 0; j < TU; ++j) {
             const int64_t i0 = base + 256 * j;
@@ -257,6 +272,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
             for (int c = 0; c < 4; ++c) {
                 const float q = pow2_n ? acc[j][c] * inv_n : acc[j][c] / fN;
                 red[c] = avg ? q : acc[j][c];
+                if constexpr (ACC) red[c] = prev[j][c] + red[c];
             }
             if constexpr (WRITE) {
                 if (full) {
@@ -288,14 +304,22 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
     const int64_t t_end = t_begin + per < nfull ? t_begin + per : nfull;
     if (t_begin < t_end) {
         RawQuad<DT> cur[KC][TU], nxt[KC][TU];
-        auto load_group = [&](RawQuad<DT> (&x)[KC][TU], int64_t tt, int gg) {
+        RawQuad<ZERO_F32> pcur[TU], pnxt[TU];   // accumulator quads (ACC only)
+        auto load_group = [&](RawQuad<DT> (&x)[KC][TU], RawQuad<ZERO_F32> (&px)[TU], int64_t tt,
+                              int gg) {
             const int64_t base = tt * kT + 4 * lane;
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk)
 #pragma unroll
                 for (int j = 0; j < TU; ++j) x[kk][j].load(a.bufs[gg * KC + kk], base + 256 * j);
+            if constexpr (ACC) {
+                if (gg == 0) {
+#pragma unroll
+                    for (int j = 0; j < TU; ++j) px[j].load(a.red_out, base + 256 * j);
+                }
+            }
         };
-        load_group(cur, t_begin, 0);
+        load_group(cur, pcur, t_begin, 0);
         int64_t t = t_begin;
         int g = 0;
         float acc[TU][4];
@@ -310,14 +334,20 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
             int64_t tn = t;
             if (gn == ngroups) { gn = 0; tn = t + 1; }
             const bool more = tn < t_end;
-            load_group(nxt, more ? tn : t, more ? gn : g);
+            load_group(nxt, pnxt, more ? tn : t, more ? gn : g);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk)                  // rank order per element
 #pragma unroll
                 for (int j = 0; j < TU; ++j) cur[kk][j].add_to(acc[j]);
             if (gn == 0) {                                   // tile t complete
-                finish(acc, t * kT + 4 * lane, true);
+                float prev[TU][4];
+#pragma unroll
+                for (int j = 0; j < TU; ++j) {
+                    prev[j][0] = pcur[j].x.x; prev[j][1] = pcur[j].x.y;
+                    prev[j][2] = pcur[j].x.z; prev[j][3] = pcur[j].x.w;
+                }
+                finish(acc, prev, t * kT + 4 * lane, true);
 #pragma unroll
                 for (int j = 0; j < TU; ++j)
 #pragma unroll
@@ -325,6 +355,9 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
             }
             if (!more) break;
             __builtin_memcpy(cur, nxt, sizeof(cur));         // register renaming
+            if constexpr (ACC) {
+                if (gn == 0) __builtin_memcpy(pcur, pnxt, sizeof(pcur));
+            }
             t = tn;
             g = gn;
         }
@@ -346,7 +379,15 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
                     if (i < n) acc[j][c] = acc[j][c] + load_one<DT>(a.bufs[k], i);
                 }
         }
-        finish(acc, base, false);
+        float prev[TU][4];
+#pragma unroll
+        for (int j = 0; j < TU; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t i = base + 256 * j + c;
+                prev[j][c] = (ACC && i < n) ? a.red_out[i] : 0.0f;
+            }
+        finish(acc, prev, base, false);
     }
     if constexpr (STATS) {
         const double mine = ss0 + ss1;
@@ -479,7 +520,7 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamLaunch a) {
     const StepScalars s = read_step(a.st, a.beta1, a.beta2, a.max_norm);
     if (s.skip) return;  // overflow on this or another rank: nothing is written
     const int lane = threadIdx.x & 63;
-    const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t wave_id = wave_index();
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const int64_t ntiles = (a.n + kTile - 1) / kTile;
     const int64_t nfull = VEC ? a.n / kTile : 0;
@@ -523,7 +564,7 @@ __global__ void finalize_kernel(zero_step_state_t* st, double beta1, double beta
 template <int DT, bool VEC>
 __global__ void __launch_bounds__(kThreads) quant_kernel(QuantLaunch a) {
     const int lane = threadIdx.x & 63;
-    const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t wave_id = wave_index();
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const int64_t n = a.n;
     const int64_t ntiles = (n + kTile - 1) / kTile;
@@ -555,6 +596,81 @@ __global__ void __launch_bounds__(kThreads) quant_kernel(QuantLaunch a) {
     }
 }
 
+// ---------------------------------------------------------------- INT8 consumer
+// out[s*S + i] = round(f32(q) * scale of (slot s, block i / block)).  A wave
+// tile is kDU slices of 256 elements of one slot (tiles never straddle slots,
+// so blocks restart at every slot start as the producer wrote them); in slice
+// u lane l owns elements 256u + 4l .. 4l+3: one 4-byte code load, one 8-byte
+// (16-bit) or 16-byte (fp32) store, each wave instruction one contiguous span.
+// The scale is a cached load shared by the lanes of a block.
+constexpr int kDU = 8;
+constexpr int64_t kDTile = 256 * kDU;
+
+template <int OT>
+__device__ __forceinline__ void store_out_quad(void* out, int64_t i, const float x[4]) {
+    if constexpr (OT == ZERO_F32) {
+        stnt_f4(static_cast<float*>(out) + i, x[0], x[1], x[2], x[3]);
+    } else {
+        stnt_u2(static_cast<uint16_t*>(out) + i, round16<OT>(x[0]) | (round16<OT>(x[1]) << 16),
+                round16<OT>(x[2]) | (round16<OT>(x[3]) << 16));
+    }
+}
+template <int OT>
+__device__ __forceinline__ void store_out_one(void* out, int64_t i, float x) {
+    if constexpr (OT == ZERO_F32) static_cast<float*>(out)[i] = x;
+    else static_cast<uint16_t*>(out)[i] = (uint16_t)round16<OT>(x);
+}
+// code c (0..3) of a little-endian 4-code word, sign-extended
+__device__ __forceinline__ float code_of(uint32_t w, int c) {
+    return (float)((int32_t)(w << (24 - 8 * c)) >> 24);
+}
+
+template <int OT, bool VEC>
+__global__ void __launch_bounds__(kThreads) dequant_kernel(DequantLaunch a, int block_shift) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_id = wave_index();
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int64_t S = a.slot_numel;
+    const int64_t per_slot = (S + kDTile - 1) / kDTile;
+    const int64_t ntiles = per_slot * a.n_slots;
+    const int64_t nb = (S + a.block - 1) / a.block;
+    auto block_of = [&](int64_t i) -> int64_t {
+        return block_shift >= 0 ? (i >> block_shift) : i / a.block;
+    };
+    for (int64_t t = wave_id; t < ntiles; t += nwaves) {
+        const int64_t slot = t / per_slot;
+        const int64_t w0 = (t - slot * per_slot) * kDTile;  // first element within the slot
+        const int8_t* q = a.q + slot * S;
+        const float* qs = a.qs + slot * nb;
+        const int64_t o0 = slot * S;
+        if (VEC && w0 + kDTile <= S) {
+            uint32_t code[kDU];
+            float sc[kDU];
+#pragma unroll
+            for (int u = 0; u < kDU; ++u) {
+                const int64_t i = w0 + 256 * u + 4 * lane;
+                code[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q + i));
+                sc[u] = qs[block_of(i)];                 // 4 | block: one block per lane quad
+            }
+#pragma unroll
+            for (int u = 0; u < kDU; ++u) {
+                float x[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[c] = code_of(code[u], c) * sc[u];
+                store_out_quad<OT>(a.out, o0 + w0 + 256 * u + 4 * lane, x);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kDU; ++u)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t i = w0 + 256 * u + 4 * lane + c;
+                    if (i < S) store_out_one<OT>(a.out, o0 + i, (float)q[i] * qs[block_of(i)]);
+                }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launch helpers
 int grid_for_tiles(int64_t ntiles, int cap) {
     int64_t g = (ntiles + kWaves - 1) / kWaves;
@@ -582,9 +698,9 @@ int resident_blocks(K kernel) {
 // The reduce grid is persistent (one partial sum per block, at most
 // ZERO_MAX_PARTIALS blocks): a whole number of resident rounds, so that no
 // partly filled last round leaves the machine idle while it drains.
-template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC>
+template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC>
 void launch_reduce_shape(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
-    auto kernel = reduce_kernel<DT, VEC, WRITE, STATS, TU, KC>;
+    auto kernel = reduce_kernel<DT, VEC, WRITE, STATS, TU, KC, ACC>;
     const int64_t ntiles = (a.n + 256 * TU - 1) / (256 * TU);
     int grid = grid_for_tiles(ntiles, kMaxGridReduce);
     const int round = resident_blocks(kernel);
@@ -593,16 +709,16 @@ void launch_reduce_shape(const ReduceLaunch& a, void* stream, float inv_n, int p
                        pow2);
 }
 
-template <int DT, bool VEC, bool WRITE, bool STATS>
+template <int DT, bool VEC, bool WRITE, bool STATS, bool ACC>
 int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     const int N = a.n_ranks;
     const int pow2 = (N & (N - 1)) == 0;
     const float inv_n = 1.0f / (float)N;  // exact when N is a power of two
     // reads in flight per lane: TU chunks x KC buffers (KC divides N)
-    if (N % 8 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 8>(a, stream, inv_n, pow2);
-    else if (N % 4 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 4>(a, stream, inv_n, pow2);
-    else if (N % 2 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 4, 2>(a, stream, inv_n, pow2);
-    else launch_reduce_shape<DT, VEC, WRITE, STATS, 8, 1>(a, stream, inv_n, pow2);
+    if (N % 8 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
+    else if (N % 4 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
+    else if (N % 2 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
+    else launch_reduce_shape<DT, VEC, WRITE, STATS, 8, 1, ACC>(a, stream, inv_n, pow2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (STATS) {
@@ -616,9 +732,13 @@ template <int DT, bool VEC>
 int launch_reduce_d(const ReduceLaunch& a, void* stream) {
     const bool write = a.red_out != nullptr;
     const bool stats = a.st != nullptr;
-    if (write && stats) return launch_reduce_t<DT, VEC, true, true>(a, stream);
-    if (write) return launch_reduce_t<DT, VEC, true, false>(a, stream);
-    return launch_reduce_t<DT, VEC, false, true>(a, stream);
+    if (write && a.accumulate) {
+        if (stats) return launch_reduce_t<DT, VEC, true, true, true>(a, stream);
+        return launch_reduce_t<DT, VEC, true, false, true>(a, stream);
+    }
+    if (write && stats) return launch_reduce_t<DT, VEC, true, true, false>(a, stream);
+    if (write) return launch_reduce_t<DT, VEC, true, false, false>(a, stream);
+    return launch_reduce_t<DT, VEC, false, true, false>(a, stream);
 }
 
 template <int DT>
@@ -676,6 +796,24 @@ int launch_adamw(const AdamLaunch& a, void* stream) {
         return (int)hipGetLastError();
     }
     return 0;
+}
+
+int launch_dequant(const DequantLaunch& a, void* stream) {
+    const int64_t per_slot = (a.slot_numel + kDTile - 1) / kDTile;
+    const int grid = grid_for_tiles(per_slot * a.n_slots, kMaxGridStream);
+    int shift = -1;
+    if ((a.block & (a.block - 1)) == 0) shift = __builtin_ctz((unsigned)a.block);
+    hipStream_t s = (hipStream_t)stream;
+#define ZF_DQ(OT)                                                                           \
+    do {                                                                                    \
+        if (a.vec) hipLaunchKernelGGL((dequant_kernel<OT, true>), dim3(grid), dim3(kThreads), 0, s, a, shift); \
+        else hipLaunchKernelGGL((dequant_kernel<OT, false>), dim3(grid), dim3(kThreads), 0, s, a, shift);      \
+    } while (0)
+    if (a.out_dtype == ZERO_F32) ZF_DQ(ZERO_F32);
+    else if (a.out_dtype == ZERO_F16) ZF_DQ(ZERO_F16);
+    else ZF_DQ(ZERO_BF16);
+#undef ZF_DQ
+    return (int)hipGetLastError();
 }
 
 int launch_quant(const QuantLaunch& a, void* stream) {

@@ -19,6 +19,7 @@ struct ReduceLaunch {
     int32_t vec;     // 1: every pointer allows 16-byte accesses
     int64_t n;
     float* red_out;  // may be null
+    int32_t accumulate;     // 1: red_out += reduce (red_out is read, then written)
     zero_step_state_t* st;  // may be null
 };
 int launch_reduce_stats(const ReduceLaunch& a, void* stream);
@@ -51,6 +52,19 @@ struct QuantLaunch {
     float* qs;
 };
 int launch_quant(const QuantLaunch& a, void* stream);
+
+// Dequantise n_slots INT8 slots of slot_numel codes into the flat buffer.
+struct DequantLaunch {
+    const int8_t* q;
+    const float* qs;
+    void* out;
+    int32_t out_dtype;
+    int32_t block;
+    int32_t n_slots;
+    int32_t vec;     // 1: slot_numel % 4 == 0 and every pointer allows quad accesses
+    int64_t slot_numel;
+};
+int launch_dequant(const DequantLaunch& a, void* stream);
 
 const char* hip_error_string(int err);
 

@@ -5,8 +5,8 @@ arithmetic happens here; every part of the step runs in libzeroflat.
 """
 import torch
 
-from . import (ZERO_AVG, StepState, zero_adamw_shard_step, zero_grad_reduce_shard,
-               zero_unscale_norm)
+from . import (ZERO_AVG, StepState, zero_adamw_shard_step, zero_grad_accumulate_shard,
+               zero_grad_reduce_shard, zero_unscale_norm)
 
 
 class ShardOptimizer:
@@ -39,6 +39,27 @@ class ShardOptimizer:
         zero_grad_reduce_shard(grad_bufs, elem_offset, self.numel, op, red, self.state,
                                stream=stream)
         self._apply(red, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
+                    q_scale_offset, stream)
+
+    def micro_step(self, grad_bufs, elem_offset, op=ZERO_AVG, first=False, last=False,
+                   stream=None):
+        """One micro-step of gradient accumulation into the fp32 gradient shard:
+        the first overwrites it (reduce), later ones add to it, and the last one
+        also takes the step statistics over the accumulated shard."""
+        red = self.reduced_buffer()
+        st = self.state if last else None
+        if first:
+            zero_grad_reduce_shard(grad_bufs, elem_offset, self.numel, op, red, st, stream=stream)
+        else:
+            zero_grad_accumulate_shard(grad_bufs, elem_offset, self.numel, op, red, st,
+                                       stream=stream)
+
+    def step_from_accumulated(self, allgather_buf, slot_offset, q_buf=None, q_scales=None,
+                              q_slot_offset=0, q_scale_offset=0, stream=None):
+        """The step on the shard accumulated by micro_step (statistics already taken)."""
+        if self._red is None:
+            raise RuntimeError("no accumulated gradient: call micro_step first")
+        self._apply(self._red, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
                     q_scale_offset, stream)
 
     def step_from_reduced(self, grad_shard, allgather_buf, slot_offset, q_buf=None,

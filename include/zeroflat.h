@@ -17,6 +17,12 @@
  *                              optional blockwise INT8 of that slot, and the
  *                              loss-scaler / step-counter update.
  *   4. zero_quant_allgather_slot  blockwise INT8 of an existing slot.
+ *   5. zero_dequant_allgather  the receiving side of the INT8 All-Gather:
+ *                              the gathered slots' codes and scales back to
+ *                              the full fp16/bf16 (or fp32) flat parameter.
+ *   6. zero_grad_accumulate_shard  gradient accumulation over micro-steps:
+ *                              reduce as in 2, added into the rank's fp32
+ *                              gradient shard.
  *
  * Sources (three web pages, cited by title and section):
  *   "DeepSpeed 与 FSDP" (docs.ifdog.com): ZeRO-1/2/3 memory arithmetic,
@@ -252,6 +258,61 @@ int zero_quant_allgather_slot(const void* slot, int32_t dtype, int64_t n, int32_
                               int8_t* q_buf, int64_t q_slot_offset, float* q_scales,
                               int64_t q_scale_offset, void* stream);
 
+/* ------------------------------------------------------------------------
+ * 5. INT8 All-Gather consumer.
+ *
+ * "DeepSpeed 与 FSDP", ZeRO++：量化通信压缩: the int8 parameter shards are
+ * dequantised by the receiver; 2kiu.com §4.2: the INT8 weights are restored
+ * only right before local compute; "DeepSpeed 与 FSDP", FSDP 的分片粒度与
+ * FlatParameter: one All-Gather returns the whole flat buffer, which is then
+ * unflattened into the parameters -- views at each parameter's [start, end)
+ * of zero_flat_layout's spans, so unflattening moves no data.
+ *
+ * The gathered payload holds n_slots rank slots of slot_numel codes each, as
+ * the producer (zero_adamw_shard_step / zero_quant_allgather_slot) wrote
+ * them: slot s's codes at q_buf[s*slot_numel ...], its scales at
+ * q_scales[s*nb ...] with nb = ceil(slot_numel/block), blocks restarting at
+ * each slot's start.  For s < n_slots, i < slot_numel, b = i / block:
+ *     out[s*slot_numel + i] = round_nearest_even_out_dtype( f32(q) * scale )
+ * with f32(q) * scale one binary32 product (exact NaN/inf rules of IEEE; a
+ * zero scale gives signed zeros).  out_dtype is ZERO_F16, ZERO_BF16 (the
+ * parameter formats) or ZERO_F32.
+ * q_buf: DEVICE int8[n_slots*slot_numel]; q_scales: DEVICE fp32[n_slots*nb],
+ *   4-byte aligned; out: DEVICE out_dtype[n_slots*slot_numel], aligned to its
+ *   element size, not aliasing the inputs.  1 <= n_slots <= 65536,
+ *   slot_numel >= 0, block a positive multiple of 4.  Any layout is accepted;
+ *   the fast path needs slot_numel % 4 == 0, q_buf 4-byte, out 8-byte (16-byte
+ *   for fp32) aligned.  Reads 1 + 4/block bytes and writes 2 (or 4) bytes per
+ *   element.
+ * ---------------------------------------------------------------------- */
+int zero_dequant_allgather(const int8_t* q_buf, const float* q_scales, int32_t n_slots,
+                           int64_t slot_numel, int32_t block, void* out, int32_t out_dtype,
+                           void* stream);
+/* ------------------------------------------------------------------------
+ * 6. Gradient accumulation in the sharded state.
+ *
+ * "DeepSpeed 与 FSDP", 实践要点: with gradient accumulation a batch is split
+ * into micro-batches whose gradients add up before one optimizer step, each
+ * micro-batch's loss divided by the number of micro-steps (so the 1/steps
+ * factor is already inside the gradients this call reads); 2kiu.com §5.3:
+ * under ZeRO the gradients accumulate in their sharded form; §5.1 sets
+ * gradient_accumulation_steps to 2.  Each micro-step reduces its N rank
+ * buffers exactly as zero_grad_reduce_shard does and adds that result into the
+ * rank's fp32 gradient shard:
+ *     acc[i] = acc[i] + red_i          (fp32, IEEE; red_i as in section 2)
+ * The first micro-step may instead call zero_grad_reduce_shard into acc (the
+ * same values as accumulating into zeros).  d_state: NULL on the earlier
+ * micro-steps; on the last one the step statistics of section 2 are taken over
+ * the accumulated shard (u_i = acc[i] * (1/loss_scale)), which is what
+ * zero_adamw_shard_step then reads: an inf/NaN from any micro-step stays
+ * non-finite in acc and is caught there.
+ * Arguments as zero_grad_reduce_shard, with acc: DEVICE fp32[shard_numel],
+ * read and written, not aliasing the inputs.  Reads 2N + 4 (16-bit inputs)
+ * and writes 4 bytes per element.
+ * ---------------------------------------------------------------------- */
+int zero_grad_accumulate_shard(const void* const* grad_bufs, int32_t n_ranks, int32_t in_dtype,
+                               int64_t elem_offset, int64_t shard_numel, int32_t op, float* acc,
+                               zero_step_state_t* d_state, void* stream);
 #ifdef __cplusplus
 }
 #endif

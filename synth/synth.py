@@ -55,6 +55,10 @@ def _cpu_lib():
         L.synth_normal_f32_at.restype = None
         L.synth_normal_f32_at.argtypes = [C.c_uint64, C.c_void_p, C.c_int64, C.c_float,
                                           C.c_void_p]
+        L.synth_codes_i8.restype = None
+        L.synth_codes_i8.argtypes = [C.c_uint64, C.c_int64, C.c_int64, C.c_void_p]
+        L.synth_codes_i8_at.restype = None
+        L.synth_codes_i8_at.argtypes = [C.c_uint64, C.c_void_p, C.c_int64, C.c_void_p]
         L.synth_mix64.restype = C.c_uint64
         L.synth_mix64.argtypes = [C.c_uint64]
         _cpu = L
@@ -70,6 +74,8 @@ def _gpu_lib():
         L.synth_fill_normal.restype = C.c_int
         L.synth_fill_normal.argtypes = [C.c_uint64, C.c_int64, C.c_int64, C.c_float,
                                         C.c_void_p, C.c_int32, C.c_void_p]
+        L.synth_fill_codes.restype = C.c_int
+        L.synth_fill_codes.argtypes = [C.c_uint64, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
         L.synth_copy.restype = C.c_int
         L.synth_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
         _gpu = L
@@ -104,6 +110,21 @@ def normal_f32_at(key, idx, sigma):
     out = np.empty(idx.size, np.float32)
     _cpu_lib().synth_normal_f32_at(key, idx.ctypes.data_as(C.c_void_p), idx.size, sigma,
                                    out.ctypes.data_as(C.c_void_p))
+    return out
+
+
+def codes(key, start, n):
+    """Integer codes in [-127, 127] for elements [start, start+n) (int8)."""
+    out = np.empty(n, np.int8)
+    _cpu_lib().synth_codes_i8(key, start, n, out.ctypes.data_as(C.c_void_p))
+    return out
+
+
+def codes_at(key, idx):
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    out = np.empty(idx.size, np.int8)
+    _cpu_lib().synth_codes_i8_at(key, idx.ctypes.data_as(C.c_void_p), idx.size,
+                                 out.ctypes.data_as(C.c_void_p))
     return out
 
 
@@ -142,6 +163,18 @@ def fill_normal(t, key, start, sigma, stream=None):
                                       _torch_code(t), C.c_void_p(s))
     if rc != 0:
         raise RuntimeError("synth_fill_normal failed: hip error %d" % rc)
+    return t
+
+
+def fill_codes(t, key, start=0, stream=None):
+    """Fill a contiguous int8 CUDA tensor with the codes of (key, start+i)."""
+    import torch
+    assert t.is_cuda and t.is_contiguous() and t.dtype == torch.int8
+    s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    rc = _gpu_lib().synth_fill_codes(key, start, t.numel(), C.c_void_p(t.data_ptr()),
+                                     C.c_void_p(s))
+    if rc != 0:
+        raise RuntimeError("synth_fill_codes failed: hip error %d" % rc)
     return t
 
 

@@ -16,6 +16,10 @@
  *       z = (2*sum(u) - 12*65535) * 2^-17      (mean 0, variance ~1, |z| <= 6)
  *   computed exactly in integers, converted exactly to binary32; the value
  *   is z * sigma rounded once to binary32.
+ *
+ * Integer codes in [-127, 127] (stand-ins for a gathered INT8 payload):
+ *   element j uses output j alone, h = mix(key + (j+1)*gamma); its high 32
+ *   bits hi give code = floor(hi * 255 / 2^32) - 127.
  */
 #include <stdint.h>
 
@@ -48,4 +52,19 @@ void synth_normal_f32(uint64_t key, int64_t start, int64_t n, float sigma, float
 /* out[i] = sigma * z(key, idx[i]) */
 void synth_normal_f32_at(uint64_t key, const int64_t* idx, int64_t n, float sigma, float* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = unit_variate(key, (uint64_t)idx[i]) * sigma;
+}
+
+static int8_t code_of(uint64_t key, uint64_t j) {
+    const uint64_t hi = mix64(key + (j + 1u) * GAMMA) >> 32;
+    return (int8_t)((int64_t)((hi * 255u) >> 32) - 127);
+}
+
+/* out[i] = code(key, start + i), i in [0, n) */
+void synth_codes_i8(uint64_t key, int64_t start, int64_t n, int8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = code_of(key, (uint64_t)(start + i));
+}
+
+/* out[i] = code(key, idx[i]) */
+void synth_codes_i8_at(uint64_t key, const int64_t* idx, int64_t n, int8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = code_of(key, (uint64_t)idx[i]);
 }

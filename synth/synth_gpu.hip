@@ -12,6 +12,8 @@
  *   (Irwin-Hall(12)): z = (2*sum - 786420) * 2^-17, exact in integers and
  *   exactly representable in binary32; value = z * sigma (one rounding),
  *   then rounded to nearest-even into the storage format (on the bits).
+ *   Integer codes in [-127, 127]: element j takes output j, hi = its high 32
+ *   bits, code = floor(hi * 255 / 2^32) - 127.
  */
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -69,6 +71,15 @@ __global__ void __launch_bounds__(256) fill_normal(uint64_t key, int64_t start, 
     }
 }
 
+__global__ void __launch_bounds__(256) fill_codes(uint64_t key, int64_t start, int64_t n,
+                                                  int8_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const uint64_t hi = mix64(key + ((uint64_t)(start + i) + 1u) * kGamma) >> 32;
+        out[i] = (int8_t)((int64_t)((hi * 255u) >> 32) - 127);
+    }
+}
+
 /* Plain streaming copy of 16-byte words: the reference kernel whose
  * FETCH_SIZE/WRITE_SIZE per byte calibrate the counters and whose time is
  * the practical read+write ceiling. */
@@ -111,6 +122,14 @@ int synth_fill_normal(uint64_t key, int64_t start, int64_t n, float sigma, void*
 }
 
 /* nbytes must be a multiple of 16 and both pointers 16-byte aligned. */
+/* out[i] = integer code of (key, start + i) in [-127, 127]. */
+int synth_fill_codes(uint64_t key, int64_t start, int64_t n, int8_t* out, void* stream) {
+    if (n <= 0) return 0;
+    hipLaunchKernelGGL(fill_codes, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, key,
+                       start, n, out);
+    return (int)hipGetLastError();
+}
+
 int synth_copy(const void* src, void* dst, int64_t nbytes, int32_t grid, void* stream) {
     if (nbytes <= 0) return 0;
     if ((nbytes & 15) || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))

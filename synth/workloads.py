@@ -43,6 +43,7 @@ class Workload:
     master_sigma: float = 0.02
     full_allgather: bool = True  # False: the slot is its own buffer (offset 0)
     inject: Optional[Tuple[int, int, int, float]] = None  # (step, rank buffer, flat index, value)
+    micro_steps: int = 1       # > 1: gradient accumulation over this many micro-steps
     hp: dict = field(default_factory=lambda: dict(HP))
 
     @property
@@ -85,7 +86,65 @@ WORKLOADS = {
     # (active); bf16 write-back plus INT8 blocks of 256; slot-sized buffers
     "70b_n64_int8": Workload("70b_n64_int8", (70_000_000_000,), 64, 63, BF16, BF16, False,
                              loss_scale=1.0, steps=5, quant_block=256, full_allgather=False),
+    # gradient accumulation (2kiu.com §5.1: gradient_accumulation_steps 2):
+    # each step reduces 2 micro-steps' rank buffers into the fp32 shard
+    "tiny_mlp_n4_accum2": Workload("tiny_mlp_n4_accum2", TINY_MLP, 4, 1, F16, F16, True,
+                                   steps=3, micro_steps=2),
+    "10b_n8_accum2": Workload("10b_n8_accum2", (10_000_000_000,), 8, 7, F16, F16, True,
+                              steps=5, micro_steps=2),
 }
+
+
+@dataclass(frozen=True)
+class Gather:
+    """The receiving side of an INT8 All-Gather: n_ranks slots of the flat
+    parameter's codes and block scales, dequantised into the full flat buffer."""
+    name: str
+    numels: Tuple[int, ...]
+    n_ranks: int
+    out_dtype: int
+    block: int = 256
+    scale_sigma: float = 4.7e-4   # ~ amax/127 of an N(0, 0.02) block
+
+    @property
+    def total(self):
+        return sum(self.numels)
+
+    @property
+    def shard(self):
+        return -(-self.total // self.n_ranks)
+
+    @property
+    def padded(self):
+        return self.shard * self.n_ranks
+
+    @property
+    def n_blocks(self):
+        return -(-self.shard // self.block)
+
+
+GATHERS = {
+    "tiny_mlp_n4_gather": Gather("tiny_mlp_n4_gather", TINY_MLP, 4, F16),
+    # one FSDP unit: the 7B block's flat parameter gathered from 8 ranks
+    "llama7b_block_n8_gather": Gather("llama7b_block_n8_gather", LLAMA7B_BLOCK, 8, BF16),
+    # the whole 70B flat parameter from 64 ranks' INT8 slots
+    "70b_n64_gather": Gather("70b_n64_gather", (70_000_000_000,), 64, BF16),
+}
+
+
+def key_codes(g):
+    from .synth import stream_key
+    return stream_key("codes", g.name)
+
+
+def key_scales(g):
+    from .synth import stream_key
+    return stream_key("scales", g.name)
+
+
+def key_grad_micro(w, step, micro, k):
+    from .synth import stream_key
+    return stream_key("grad", w.name, step, "micro", micro, k)
 
 
 def key_grad(w, step, k):

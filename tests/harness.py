@@ -41,6 +41,27 @@ def assert_bitwise(got, ref, what):
                              % (what, bad.size, g.size, i, got[i], ref[i]))
 
 
+def is_nan(a, code):
+    """NaN mask of float32 values (code 0) or 16-bit bit patterns (1 fp16, 2 bf16)."""
+    a = np.asarray(a)
+    if code == 0:
+        return np.isnan(a)
+    exp, man = (0x7C00, 0x03FF) if code == 1 else (0x7F80, 0x007F)
+    return ((a & exp) == exp) & ((a & man) != 0)
+
+
+def assert_bitwise_nan_class(got, ref, code, what):
+    """Bit-exact, except that NaN results only have to be NaN: IEEE 754 leaves
+    the sign of the NaN of an invalid operation (0 * inf) to the platform."""
+    ng, nr = is_nan(got, code), is_nan(ref, code)
+    bad = np.nonzero(ng != nr)[0]
+    assert bad.size == 0, "%s: NaN at different places, first %d" % (what, int(bad[0]))
+    g, r = bits(got).copy(), bits(ref).copy()
+    g[ng] = 0
+    r[nr] = 0
+    assert_bitwise(g, r, what)
+
+
 def ulp16_distance(a, b):
     """|ord(a) - ord(b)| for 16-bit float bit patterns (sign-magnitude order)."""
     def order(x):

@@ -139,3 +139,43 @@ def test_step_calls_validate_before_launch(zf):
     assert L.zero_quant_allgather_slot(p, 1, 16, 64, p, 0, p, 0, None) == -1
     assert L.zero_quant_allgather_slot(C.c_void_p(0x1001), 1, 16, 256, p, 0, p, 0, None) == -2
     assert b"block" in L.zero_last_error() or L.zero_last_error()
+
+
+def test_consumer_and_accumulate_validate_before_launch(zf):
+    L = zf.lib()
+    p = C.c_void_p(0x1000)
+    assert L.zero_dequant_allgather(p, p, 4, 256, 256, p, 7, None) == -1          # bad dtype
+    assert L.zero_dequant_allgather(p, p, 0, 256, 256, p, 2, None) == -3          # no slots
+    assert L.zero_dequant_allgather(p, p, 65537, 256, 256, p, 2, None) == -3
+    assert L.zero_dequant_allgather(p, p, 4, -1, 256, p, 2, None) == -1
+    assert L.zero_dequant_allgather(p, p, 4, 256, 6, p, 2, None) == -1            # block % 4
+    assert L.zero_dequant_allgather(p, p, 4, 256, 0, p, 2, None) == -1
+    assert L.zero_dequant_allgather(None, p, 4, 256, 256, p, 2, None) == -1
+    assert L.zero_dequant_allgather(p, C.c_void_p(0x1002), 4, 256, 256, p, 2, None) == -2
+    assert L.zero_dequant_allgather(p, p, 4, 256, 256, C.c_void_p(0x1001), 2, None) == -2
+    assert L.zero_dequant_allgather(p, p, 4, 256, 256, C.c_void_p(0x1002), 0, None) == -2
+    assert L.zero_dequant_allgather(p, p, 2, 1 << 62, 256, p, 2, None) == -3      # overflow
+    assert L.zero_dequant_allgather(None, None, 4, 0, 256, None, 2, None) == 0   # empty: no-op
+    bufs = (C.c_void_p * 1)(0x1000)
+    assert L.zero_grad_accumulate_shard(bufs, 0, 1, 0, 8, 0, p, None, None) == -3
+    assert L.zero_grad_accumulate_shard(bufs, 1, 1, 0, 8, 3, p, None, None) == -1
+    assert L.zero_grad_accumulate_shard(bufs, 1, 1, 0, 8, 0, None, None, None) == -1
+    assert L.zero_grad_accumulate_shard(bufs, 1, 1, 0, 8, 0, C.c_void_p(0x1002), None, None) == -2
+    assert b"zero_grad_accumulate_shard" in L.zero_last_error()
+    assert L.zero_grad_accumulate_shard(bufs, 1, 1, 0, 0, 0, p, None, None) == 0  # empty: no-op
+
+
+def test_unflatten_views_follow_the_layout(zf):
+    """Views at the spans zero_flat_layout gives: the flat buffer is the
+    parameters back to back, each view a reshape of its range (no copy)."""
+    import torch
+    shapes = [(512, 1024), (1024,), (1024, 512), (512,)]
+    flat = torch.arange(1_050_112 + 3, dtype=torch.float32)       # + tail padding
+    views = zf.unflatten(flat, shapes, n_ranks=4)
+    off = 0
+    for v, sh in zip(views, shapes):
+        assert tuple(v.shape) == sh and v.data_ptr() == flat.data_ptr() + 4 * off
+        assert v.flatten()[0].item() == off
+        off += v.numel()
+    with pytest.raises(ValueError):
+        zf.unflatten(torch.zeros(10), shapes)
