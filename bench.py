@@ -12,7 +12,13 @@ A "step" is the whole path: statistics kernel + fold, the AdamW kernel, and
 the loss-scaler finalize.  The AdamW kernel is the dominant one; its duration
 is taken with HIP events on the launch stream around every launch.
 
-Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Also timed, each as whole steps: the other workloads (8- and 64-way reduces,
+the 70B INT8 shard, the 7B block, the Tiny MLP, gradient accumulation over 2
+micro-steps), and the INT8 All-Gather consumer (gathered slots dequantised into
+the full flat parameter) on the 7B block and the whole 70B flat parameter.
+
+Prints ONE JSON line.  --gpus N with N > 1 exits: the library runs one rank's
+step on one GPU.
 """
 import argparse
 import hashlib
@@ -40,6 +46,14 @@ VARIANTS = (   # the other workloads, whole steps each (parity cases in tests/ a
     ("llama7b_block_n8", "Llama-7B block (2.02e8 params)/8 rank-3 shard, 8 bf16 rank slices (AVG)"),
     ("tiny_mlp_n4", "2-layer MLP (1.05e6 params)/4 rank-0 shard, 4 fp16 rank slices (AVG); "
                     "cache-resident and launch-bound"),
+    ("10b_n8_accum2", "10B/8 rank-7 shard, gradient accumulation over 2 micro-steps: each "
+                      "reduces 8 fp16 rank slices (AVG) into the fp32 shard, then the step"),
+)
+GATHER_VARIANTS = (   # the INT8 All-Gather consumer: gathered slots -> full flat parameter
+    ("llama7b_block_n8_gather", "Llama-7B block flat parameter (2.02e8) from 8 INT8 slots "
+                                "(block 256) to bf16"),
+    ("70b_n64_gather", "the whole 70B flat parameter (7e10) from 64 INT8 slots (block 256) "
+                       "to bf16"),
 )
 
 
@@ -162,6 +176,8 @@ def step_bytes_per_param(w):
     g16 = 2
     if w.reduce:
         stats_and_reduce = g16 * w.n_ranks + 4          # N reads, fp32 reduced shard written
+        # later micro-steps also read the accumulated fp32 shard back
+        stats_and_reduce += (w.micro_steps - 1) * (g16 * w.n_ranks + 8)
         adam_grad = 4                                   # the fp32 reduced shard read back
     else:
         stats_and_reduce = g16                          # statistics pass over the 16-bit shard
@@ -175,7 +191,7 @@ def step_bytes_per_param(w):
 def run_workload(zf, torch, w, steps, warmup):
     """Whole steps of any workload (inputs generated on the GPU first)."""
     from synth import synth
-    from synth.workloads import key_grad, key_grad_reduced, key_master
+    from synth.workloads import key_grad, key_grad_micro, key_grad_reduced, key_master
     S, dev = w.shard, torch.device("cuda:0")
     gdt = torch.float16 if w.grad_dtype == 1 else torch.bfloat16
     pdt = torch.float16 if w.param_dtype == 1 else torch.bfloat16
@@ -183,7 +199,16 @@ def run_workload(zf, torch, w, steps, warmup):
     synth.fill_normal(master, key_master(w), w.start, w.master_sigma)
     opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic,
                             window=w.window, quant_block=w.quant_block)
-    if w.reduce:
+    if w.micro_steps > 1:
+        # per micro-step, the rank-r slices of the N ranks' gradient buffers
+        grads = []
+        for mi in range(w.micro_steps):
+            grads.append([])
+            for k in range(w.n_ranks):
+                b = torch.empty(S, dtype=gdt, device=dev)
+                synth.fill_normal(b, key_grad_micro(w, 0, mi, k), w.start, w.grad_sigma)
+                grads[mi].append(b)
+    elif w.reduce:
         # rank-r slices of the N ranks' gradient buffers (slot-sized, offset 0)
         grads = []
         for k in range(w.n_ranks):
@@ -204,7 +229,11 @@ def run_workload(zf, torch, w, steps, warmup):
     torch.cuda.synchronize()
 
     def one():
-        if w.reduce:
+        if w.micro_steps > 1:
+            for mi in range(w.micro_steps):
+                opt.micro_step(grads[mi], 0, op=w.op, first=mi == 0, last=mi == w.micro_steps - 1)
+            opt.step_from_accumulated(ag, off, q_buf=q, q_scales=qs)
+        elif w.reduce:
             opt.step_from_rank_buffers(grads, 0, ag, off, op=w.op, q_buf=q, q_scales=qs)
         else:
             opt.step_from_reduced(grads, ag, off, q_buf=q, q_scales=qs)
@@ -228,6 +257,49 @@ def run_workload(zf, torch, w, steps, warmup):
             "step_frac_of_peak": bpp * S / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
 
+def run_gather(zf, torch, g, steps, warmup):
+    """The INT8 All-Gather consumer on a gathered payload resident in HBM:
+    every launch dequantises all n_ranks slots into the full flat buffer."""
+    from synth import synth
+    from synth.workloads import key_codes, key_scales
+    out_dt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[g.out_dtype]
+    es = torch.empty(0, dtype=out_dt).element_size()
+    n_sc = g.n_ranks * g.n_blocks
+    need = g.padded * (1 + es) + 4 * n_sc
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    if free < need + (2 << 30):
+        return {"skipped": "needs %.1f GB of device memory, %.1f GB free" % (need / 1e9, free / 1e9)}
+    q = torch.empty(g.padded, dtype=torch.int8, device="cuda")
+    synth.fill_codes(q, key_codes(g))
+    sc = torch.empty(n_sc, device="cuda")
+    synth.fill_normal(sc, key_scales(g), 0, g.scale_sigma)
+    sc.abs_()
+    out = torch.empty(g.padded, dtype=out_dt, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        zf.zero_dequant_allgather(q, sc, g.n_ranks, g.shard, out, block=g.block)
+    ev = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        zf.zero_dequant_allgather(q, sc, g.n_ranks, g.shard, out, block=g.block)
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    del q, sc, out
+    torch.cuda.empty_cache()
+    gbps = need / (ms * 1e-3) / 1e9
+    return {"ms_per_launch": ms, "wall_ms_per_launch": wall / steps * 1e3,
+            "params_per_s": g.padded / (ms * 1e-3), "bytes_per_launch": need,
+            "bytes_per_param": need / g.padded, "GBps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS}
+
+
 def run_copy_calibration(torch, nbytes=4 << 30, reps=3):
     from synth import synth
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -247,7 +319,7 @@ def run_copy_calibration(torch, nbytes=4 << 30, reps=3):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the rank's step on a single MI355X "
+        print("bench.py measures one GPU: the library runs one rank's step on a single MI355X "
               "(the other ranks are buffers in the same HBM); --gpus %d is not supported."
               % args.gpus, file=sys.stderr)
         sys.exit(2)
@@ -300,6 +372,12 @@ def main():
             r = run_workload(zf, torch, WORKLOADS[name], max(3, args.steps // 2), 2)
             r["what"] = what
             out["variants"][name] = r
+        from synth.workloads import GATHERS
+        out["allgather_consumer"] = {}
+        for name, what in GATHER_VARIANTS:
+            r = run_gather(zf, torch, GATHERS[name], max(3, args.steps // 4), 1)
+            r["what"] = what
+            out["allgather_consumer"][name] = r
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
