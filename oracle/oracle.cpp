@@ -227,6 +227,28 @@ void oracle_reduce_accumulate(const void* const* bufs, int32_t n_ranks, int32_t 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Quantised gradient reduce.                                                */
+/* [DS] "ZeRO++：量化通信压缩": gradients travel through the Reduce-Scatter */
+/* in a quantised form (its QG scheme), cutting that collective's volume.   */
+/* The page gives no scheme; reading: every rank sends its slice for this   */
+/* rank as INT8 codes with one fp32 scale per block (the parameter          */
+/* payload's scheme, blocks restarting at the slice start), and this rank   */
+/* dequantises each rank's value, f32(q) * scale (one binary32 product),    */
+/* and sums them in rank order in fp32; AVG divides the sum by N.           */
+/* ------------------------------------------------------------------------ */
+void oracle_reduce_q8(const int8_t* const* q, const float* const* scales, int32_t n_ranks,
+                      int64_t n, int32_t block, int32_t op, float* red) {
+    for (int64_t i = 0; i < n; ++i) {
+        float acc = 0.0f;
+        for (int32_t k = 0; k < n_ranks; ++k) {
+            const float x = (float)q[k][i] * scales[k][i / block];
+            acc = acc + x;
+        }
+        red[i] = (op == OR_AVG) ? acc / (float)n_ranks : acc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Unscale, overflow test, local sum of squares.                             */
 /* [RD] §5.1 (fp16 loss scaling, initial scale 2^16) and §5.3 (overflow is  */
 /* detected on the gradients; clipping uses the global gradient norm).      */

@@ -77,6 +77,13 @@ void oracle_reduce(const void* const* bufs, int32_t n_ranks, int32_t dtype,
 void oracle_reduce_accumulate(const void* const* bufs, int32_t n_ranks, int32_t dtype,
                               int64_t offset, int64_t n, int32_t op, float* acc);
 
+/* Quantised gradient reduce: rank k's slice arrives as INT8 codes q[k][0..n)
+ * with fp32 scales scales[k][i / block];
+ *   red[i] = sum_k f32(q[k][i]) * scales[k][i / block]  (rank order, fp32),
+ * AVG divides the sum by N. */
+void oracle_reduce_q8(const int8_t* const* q, const float* const* scales, int32_t n_ranks,
+                      int64_t n, int32_t block, int32_t op, float* red);
+
 /* Unscale + overflow + local sum of squares over g[0..n):
  *   u_i = f32(g_i) * f32(1/loss_scale); overflow |= !isfinite(u_i);
  *   sumsq += (double)u_i * (double)u_i, in index order. */

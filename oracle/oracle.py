@@ -96,6 +96,9 @@ def lib():
         L.oracle_dequant_int8.restype = None
         L.oracle_dequant_int8.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64,
                                           C.c_int32, C.c_int32, C.c_void_p]
+        L.oracle_reduce_q8.restype = None
+        L.oracle_reduce_q8.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int32,
+                                       C.c_int32, C.c_void_p]
         L.oracle_scaler_update.restype = None
         L.oracle_scaler_update.argtypes = [C.POINTER(Scaler), C.c_int32]
         _lib = L
@@ -202,6 +205,20 @@ def reduce_accumulate(bufs, dtype, offset, n, op, acc):
     arr = (C.c_void_p * len(bufs))(*[b.ctypes.data for b in bufs])
     lib().oracle_reduce_accumulate(arr, len(bufs), dtype, offset, n, op, _ptr(acc))
     return acc
+
+
+def reduce_q8(qs, scales, n, block, op):
+    """red[i] = sum_k f32(qs[k][i]) * scales[k][i // block] (rank order); AVG / N."""
+    assert len(qs) == len(scales)
+    for q, sc in zip(qs, scales):
+        _check(q, np.int8)
+        _check(sc, np.float32)
+        assert q.size >= n and sc.size >= (n + block - 1) // block
+    qa = (C.c_void_p * len(qs))(*[q.ctypes.data for q in qs])
+    sa = (C.c_void_p * len(qs))(*[sc.ctypes.data for sc in scales])
+    red = np.empty(n, np.float32)
+    lib().oracle_reduce_q8(qa, sa, len(qs), n, block, op, _ptr(red))
+    return red
 
 
 def unscale_stats(g, dtype, loss_scale, sumsq=0.0, overflow=0):

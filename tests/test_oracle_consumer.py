@@ -209,3 +209,90 @@ def test_accumulated_overflow_persists(orc):
     orc.reduce_accumulate([a, a], orc.F16, 0, n, orc.AVG, acc)
     _, ovf = orc.unscale_stats(acc, orc.F32, 1.0)
     assert ovf == 1 and np.isinf(acc[9]) and np.isfinite(np.delete(acc, 9)).all()
+
+
+# ------------------------------------------------------------------ quantised gradient reduce
+# "DeepSpeed 与 FSDP", ZeRO++：量化通信压缩: gradients cross the Reduce-Scatter in a
+# quantised form; the reading takes the parameter payload's INT8 block scheme.
+def test_reduce_q8_exact_sums(orc):
+    """Power-of-two scales: every product and sum is exact, so the reduce is
+    the rational sum (AVG: divided by N)."""
+    rng = np.random.default_rng(41)
+    N, n, blk = 8, 700, 256
+    nb = -(-n // blk)
+    qs = [rng.integers(-127, 128, n).astype(np.int8) for _ in range(N)]
+    ks = [rng.integers(-12, -3, nb) for _ in range(N)]
+    scs = [np.ldexp(np.ones(nb), k).astype(np.float32) for k in ks]
+    for op in (orc.SUM, orc.AVG):
+        red = orc.reduce_q8(qs, scs, n, blk, op)
+        for i in range(0, n, 37):
+            want = sum(Fr(int(qs[k][i])) * Fr(2) ** int(ks[k][i // blk]) for k in range(N))
+            if op == orc.AVG:
+                want /= N
+            assert Fr(float(red[i])) == want
+
+
+def test_reduce_q8_block_indexing_hand_table(orc):
+    """2 ranks, 300 codes of 1, blocks of 256: rank k's block b has scale
+    2^-(2k+b+1); element i in block b reduces to 2^-(b+1) + 2^-(b+3)."""
+    n = 300
+    qs = [np.ones(n, np.int8), np.ones(n, np.int8)]
+    scs = [np.array([0.5, 0.25], np.float32), np.array([0.125, 0.0625], np.float32)]
+    red = orc.reduce_q8(qs, scs, n, 256, orc.SUM)
+    want = np.array([0.5 + 0.125] * 256 + [0.25 + 0.0625] * 44, np.float32)
+    assert np.array_equal(red, want)
+
+
+def test_reduce_q8_is_rank_ordered(orc):
+    """Codes 1 with scales 2^24, 1, 1: in rank order 2^24 + 1 rounds back to
+    2^24 twice; summed the other way round it would give 2^24 + 2."""
+    qs = [np.ones(1, np.int8)] * 3
+    scs = [np.array([2.0 ** 24], np.float32), np.ones(1, np.float32), np.ones(1, np.float32)]
+    assert float(orc.reduce_q8(qs, scs, 1, 256, orc.SUM)[0]) == 2.0 ** 24
+
+
+def test_reduce_q8_equals_dequantise_then_reduce(orc):
+    """Random codes and scales: the quantised reduce equals dequantising each
+    rank's slice (pinned above) to fp32 and reducing those buffers (pinned in
+    test_oracle_step) -- element by element, bitwise."""
+    rng = np.random.default_rng(42)
+    N, n, blk = 5, 1000, 64
+    nb = -(-n // blk)
+    qs = [rng.integers(-127, 128, n).astype(np.int8) for _ in range(N)]
+    scs = [(np.abs(rng.standard_normal(nb)) * 1e-3).astype(np.float32) for _ in range(N)]
+    deq = [orc.dequant_int8(q, sc, 1, n, blk, orc.F32) for q, sc in zip(qs, scs)]
+    for op in (orc.SUM, orc.AVG):
+        assert np.array_equal(orc.reduce_q8(qs, scs, n, blk, op).view(np.uint32),
+                              orc.reduce(deq, orc.F32, 0, n, op).view(np.uint32))
+
+
+def test_reduce_q8_error_bound_vs_the_fp16_reduce(orc):
+    """Each rank quantises its fp16 slice (the pinned quantiser); the quantised
+    reduce stays within the sum of the ranks' half quantisation steps (/N for
+    AVG), plus binary32 rounding, of the plain fp16 reduce."""
+    rng = np.random.default_rng(43)
+    N, n, blk = 8, 256 * 6 + 77, 256
+    xs = [orc.from_f32((rng.standard_normal(n) * 1e-3).astype(np.float32), orc.F16)
+          for _ in range(N)]
+    pay = [orc.quant_int8(x, orc.F16, blk) for x in xs]
+    for op, div in ((orc.SUM, 1), (orc.AVG, N)):
+        red_q = orc.reduce_q8([p[0] for p in pay], [p[1] for p in pay], n, blk, op)
+        red = orc.reduce(xs, orc.F16, 0, n, op)
+        step = sum(np.repeat(p[1].astype(np.float64), blk)[:n] for p in pay)
+        bound = step * (0.5 + 2.0 ** -15) / div + np.abs(red.astype(np.float64)) * 2.0 ** -21
+        assert np.all(np.abs(red_q.astype(np.float64) - red) <= bound)
+
+
+def test_reduce_q8_overflow_reaches_the_flag(orc):
+    """A rank whose slice held +inf sent scale inf (codes 0 for the finite
+    values): its products are NaN, so the reduce is non-finite and the
+    overflow test fires."""
+    n = 256
+    x = f16(np.full(n, 1e-3))
+    x[5] = 0x7C00
+    q, sc = orc.quant_int8(x, orc.F16, 256)
+    assert np.isinf(sc[0])
+    q2, sc2 = orc.quant_int8(f16(np.full(n, 2e-3)), orc.F16, 256)
+    red = orc.reduce_q8([q2, q], [sc2, sc], n, 256, orc.AVG)
+    assert not np.isfinite(red).any()
+    assert orc.unscale_stats(red, orc.F32, 65536.0)[1] == 1

@@ -104,6 +104,16 @@ MUTANTS = [
      "        acc[i] = acc[i] + red;",
      "        for (int32_t k = 0; k < n_ranks; ++k) acc[i] = acc[i] + load_elem(bufs[k], dtype, "
      "offset + i);", CONS),
+    ("q8_scales_of_rank0", "const float x = (float)q[k][i] * scales[k][i / block];",
+     "const float x = (float)q[k][i] * scales[0][i / block];", CONS),
+    ("q8_block_fixed_256", "const float x = (float)q[k][i] * scales[k][i / block];",
+     "const float x = (float)q[k][i] * scales[k][i / 256];", CONS),
+    ("q8_divides", "const float x = (float)q[k][i] * scales[k][i / block];",
+     "const float x = (float)q[k][i] / scales[k][i / block];", CONS),
+    ("q8_reverse_order", "for (int32_t k = 0; k < n_ranks; ++k) {\n            const float x",
+     "for (int32_t k = n_ranks - 1; k >= 0; --k) {\n            const float x", CONS),
+    ("q8_avg_missing", "acc = acc + x;\n        }\n        red[i] = (op == OR_AVG) ? acc / (float)n_ranks : acc;",
+     "acc = acc + x;\n        }\n        red[i] = acc;", CONS),
     ("accumulate_avg_ignored",
      "oracle_reduce(bufs, n_ranks, dtype, offset + i, 1, op, &red);",
      "oracle_reduce(bufs, n_ranks, dtype, offset + i, 1, OR_SUM, &red);", CONS),
