@@ -48,6 +48,10 @@ VARIANTS = (   # the other workloads, whole steps each (parity cases in tests/ a
                     "cache-resident and launch-bound"),
     ("10b_n8_accum2", "10B/8 rank-7 shard, gradient accumulation over 2 micro-steps: each "
                       "reduces 8 fp16 rank slices (AVG) into the fp32 shard, then the step"),
+    ("10b_n8_qg", "10B/8 rank-7 shard, the 8 ranks' gradient slices arriving INT8-quantised "
+                  "(blocks of 256, quantised before timing) and reduced (AVG), then the step"),
+    ("gpt1p5b_n64_qg", "1.5B/64 rank-0 shard, 64 INT8-quantised rank gradient slices reduced "
+                       "(AVG), dynamic scale"),
 )
 GATHER_VARIANTS = (   # the INT8 All-Gather consumer: gathered slots -> full flat parameter
     ("llama7b_block_n8_gather", "Llama-7B block flat parameter (2.02e8) from 8 INT8 slots "
@@ -174,7 +178,10 @@ def run_prereduced(zf, torch, w, steps, warmup):
 def step_bytes_per_param(w):
     """Algorithmic HBM bytes of one whole step per shard parameter."""
     g16 = 2
-    if w.reduce:
+    if w.grad_int8:
+        stats_and_reduce = (1 + 4.0 / 256) * w.n_ranks + 4   # N INT8 payloads, fp32 shard written
+        adam_grad = 4
+    elif w.reduce:
         stats_and_reduce = g16 * w.n_ranks + 4          # N reads, fp32 reduced shard written
         # later micro-steps also read the accumulated fp32 shard back
         stats_and_reduce += (w.micro_steps - 1) * (g16 * w.n_ranks + 8)
@@ -199,7 +206,20 @@ def run_workload(zf, torch, w, steps, warmup):
     synth.fill_normal(master, key_master(w), w.start, w.master_sigma)
     opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic,
                             window=w.window, quant_block=w.quant_block)
-    if w.micro_steps > 1:
+    if w.grad_int8:
+        # each rank's fp16 slice quantised by the library (the sender's side,
+        # outside the timed step): codes + one scale per 256 elements
+        grads = ([], [])
+        tmp = torch.empty(S, dtype=gdt, device=dev)
+        for k in range(w.n_ranks):
+            synth.fill_normal(tmp, key_grad(w, 0, k), w.start, w.grad_sigma)
+            q_k = torch.empty(S, dtype=torch.int8, device=dev)
+            s_k = torch.empty(-(-S // 256), dtype=torch.float32, device=dev)
+            zf.zero_quant_allgather_slot(tmp, q_k, s_k)
+            grads[0].append(q_k)
+            grads[1].append(s_k)
+        del tmp
+    elif w.micro_steps > 1:
         # per micro-step, the rank-r slices of the N ranks' gradient buffers
         grads = []
         for mi in range(w.micro_steps):
@@ -229,7 +249,9 @@ def run_workload(zf, torch, w, steps, warmup):
     torch.cuda.synchronize()
 
     def one():
-        if w.micro_steps > 1:
+        if w.grad_int8:
+            opt.step_from_int8_grads(grads[0], grads[1], ag, off, op=w.op, q_buf=q, q_scales=qs)
+        elif w.micro_steps > 1:
             for mi in range(w.micro_steps):
                 opt.micro_step(grads[mi], 0, op=w.op, first=mi == 0, last=mi == w.micro_steps - 1)
             opt.step_from_accumulated(ag, off, q_buf=q, q_scales=qs)

@@ -22,7 +22,8 @@ ZERO_MAX_PARTIALS = 2048
 
 EXPORTS = ("zero_last_error", "zero_flat_layout", "zero_step_state_init",
            "zero_grad_reduce_shard", "zero_unscale_norm", "zero_adamw_shard_step",
-           "zero_quant_allgather_slot", "zero_dequant_allgather", "zero_grad_accumulate_shard")
+           "zero_quant_allgather_slot", "zero_dequant_allgather", "zero_grad_accumulate_shard",
+           "zero_grad_reduce_shard_int8")
 
 
 class zero_span_t(C.Structure):
@@ -82,6 +83,8 @@ def _load():
     L.zero_dequant_allgather.argtypes = [vp, vp, i32, i64, i32, vp, i32, vp]
     L.zero_grad_accumulate_shard.restype = C.c_int
     L.zero_grad_accumulate_shard.argtypes = [vp, i32, i32, i64, i64, i32, vp, vp, vp]
+    L.zero_grad_reduce_shard_int8.restype = C.c_int
+    L.zero_grad_reduce_shard_int8.argtypes = [vp, vp, i32, i64, i32, i32, vp, vp, vp]
     return L
 
 
@@ -276,6 +279,32 @@ def zero_quant_allgather_slot(slot, q_buf, q_scales, q_slot_offset=0, q_scale_of
                                           _stream(stream)))
 
 
+
+
+def zero_grad_reduce_shard_int8(q_slices, scale_slices, shard_numel, op, red_out, state=None,
+                                block=256, stream=None):
+    """red_out[i] = sum_k f32(q_slices[k][i]) * scale_slices[k][i // block] (rank
+    order), AVG -> / N: the reduce over the N ranks' INT8-quantised gradient
+    slices for this rank; statistics into `state` when given."""
+    import torch
+    if not q_slices or len(q_slices) != len(scale_slices):
+        raise ValueError("need one codes and one scales tensor per rank")
+    nb = (shard_numel + block - 1) // block
+    for k, (q, sc) in enumerate(zip(q_slices, scale_slices)):
+        _contig(q, "q_slices[%d]" % k)
+        _contig(sc, "scale_slices[%d]" % k)
+        if q.dtype != torch.int8 or sc.dtype != torch.float32:
+            raise ValueError("codes must be int8 and scales float32")
+        if q.numel() < shard_numel or sc.numel() < nb:
+            raise ValueError("rank %d's payload is shorter than the shard" % k)
+    _contig(red_out, "red_out")
+    if _dtype_code(red_out) != ZERO_F32 or red_out.numel() < shard_numel:
+        raise ValueError("red_out must be float32 with >= shard_numel elements")
+    n = len(q_slices)
+    qa = (C.c_void_p * n)(*[q.data_ptr() for q in q_slices])
+    sa = (C.c_void_p * n)(*[sc.data_ptr() for sc in scale_slices])
+    _check(_lib.zero_grad_reduce_shard_int8(qa, sa, n, shard_numel, block, op, _ptr(red_out),
+                                            _state_ptr(state), _stream(stream)))
 
 
 # ------------------------------------------------------------------ All-Gather consumer

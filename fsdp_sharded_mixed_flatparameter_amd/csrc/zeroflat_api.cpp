@@ -327,6 +327,46 @@ int zero_quant_allgather_slot(const void* slot, int32_t dtype, int64_t n, int32_
 }
 
 // ---------------------------------------------------------------------------
+// Quantised gradient reduce ("DeepSpeed 与 FSDP", ZeRO++：量化通信压缩).
+int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const* scale_bufs,
+                                int32_t n_ranks, int64_t shard_numel, int32_t block, int32_t op,
+                                float* red_out, zero_step_state_t* d_state, void* stream) {
+    const char* fn = "zero_grad_reduce_shard_int8";
+    if (!q_bufs || !scale_bufs) return fail(ZERO_EINVAL, "%s: NULL pointer table", fn);
+    if (n_ranks < 1 || n_ranks > ZERO_MAX_RANKS / 2)
+        return fail(ZERO_ERANGE, "%s: n_ranks %d not in [1, %d]", fn, n_ranks, ZERO_MAX_RANKS / 2);
+    if (op != ZERO_SUM && op != ZERO_AVG) return fail(ZERO_EINVAL, "%s: bad op %d", fn, op);
+    if (shard_numel < 0) return fail(ZERO_EINVAL, "%s: negative size", fn);
+    if (block < 4 || block % 4 != 0) return fail(ZERO_EINVAL, "%s: block %d is not a positive multiple of 4", fn, block);
+    if (!red_out) return fail(ZERO_EINVAL, "%s: red_out is NULL", fn);
+    if (!aligned(red_out, 4)) return fail(ZERO_EALIGN, "%s: red_out not 4-byte aligned", fn);
+    if (d_state && !aligned(d_state, 8)) return fail(ZERO_EALIGN, "%s: state not 8-byte aligned", fn);
+    zf::ReduceLaunch a;
+    memset(&a, 0, sizeof a);
+    bool vec = aligned(red_out, 16);
+    for (int32_t k = 0; k < n_ranks; ++k) {
+        if (!q_bufs[k] || !scale_bufs[k]) return fail(ZERO_EINVAL, "%s: rank %d's payload is NULL", fn, k);
+        if (!aligned(scale_bufs[k], 4)) return fail(ZERO_EALIGN, "%s: scale_bufs[%d] misaligned", fn, k);
+        a.bufs[2 * k] = q_bufs[k];
+        a.bufs[2 * k + 1] = scale_bufs[k];
+        vec = vec && aligned(q_bufs[k], 4);
+    }
+    if (shard_numel == 0) return ok();
+    a.n_ranks = n_ranks;
+    a.dtype = ZERO_F32;  // unused by the INT8 source
+    a.op = op;
+    a.vec = vec ? 1 : 0;
+    a.n = shard_numel;
+    a.red_out = red_out;
+    a.block = block;
+    a.block_shift = (block & (block - 1)) == 0 ? __builtin_ctz((unsigned)block) : -1;
+    a.st = d_state;
+    const int e = zf::launch_reduce_q8(a, stream);
+    if (e) return hip_fail(e, fn);
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
 // INT8 All-Gather consumer ("DeepSpeed 与 FSDP", ZeRO++：量化通信压缩;
 // 2kiu.com §4.2): the gathered slots back to the flat parameter.
 int zero_dequant_allgather(const int8_t* q_buf, const float* q_scales, int32_t n_slots,

@@ -212,29 +212,69 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // storing a finished tile; a scheduling barrier keeps the compiler from sinking
 // them.  KC divides N (chosen by the launcher), so no group is partial and the
 // loop body has no per-buffer branches.
+//
+// Sources: a RawQuad<DT> holds one lane's four inputs of one rank buffer as
+// loaded (load) and adds their values to the accumulators (add_to); one()
+// gives a single element for the ragged tail.  DT is the buffer format, or
+// kQ8: INT8 codes with one fp32 scale per block (the quantised-gradient
+// Reduce-Scatter payload), rank k's codes at bufs[2k] and scales at bufs[2k+1];
+// its value is f32(code) * scale, one binary32 product.
+constexpr int kQ8 = 3;
+
+__device__ __forceinline__ int64_t block_of(const ReduceLaunch& a, int64_t i) {
+    return a.block_shift >= 0 ? (i >> a.block_shift) : i / a.block;
+}
+
 template <int DT>
 struct RawQuad;
 template <>
 struct RawQuad<ZERO_F32> {
     v4f x;
-    __device__ __forceinline__ void load(const void* p, int64_t i) {
-        x = ldnt_f4(static_cast<const float*>(p) + i);
+    __device__ __forceinline__ void load_ptr(const float* p, int64_t i) { x = ldnt_f4(p + i); }
+    __device__ __forceinline__ void load(const ReduceLaunch& a, int k, int64_t i, int64_t) {
+        load_ptr(static_cast<const float*>(a.bufs[k]), i);
     }
     __device__ __forceinline__ void add_to(float acc[4]) const {
         acc[0] = acc[0] + x.x; acc[1] = acc[1] + x.y; acc[2] = acc[2] + x.z; acc[3] = acc[3] + x.w;
+    }
+    __device__ static __forceinline__ float one(const ReduceLaunch& a, int k, int64_t i) {
+        return static_cast<const float*>(a.bufs[k])[i];
+    }
+};
+template <>
+struct RawQuad<kQ8> {
+    uint32_t w;  // four codes
+    float s;     // their block's scale (4 | block: a quad never straddles blocks)
+    // bi: the block of element i, the same for every rank (computed once per chunk)
+    __device__ __forceinline__ void load(const ReduceLaunch& a, int k, int64_t i, int64_t bi) {
+        w = __builtin_nontemporal_load(
+            reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(a.bufs[2 * k]) + i));
+        s = static_cast<const float*>(a.bufs[2 * k + 1])[bi];
+    }
+    __device__ __forceinline__ void add_to(float acc[4]) const {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            acc[c] = acc[c] + (float)((int32_t)(w << (24 - 8 * c)) >> 24) * s;
+    }
+    __device__ static __forceinline__ float one(const ReduceLaunch& a, int k, int64_t i) {
+        return (float)static_cast<const int8_t*>(a.bufs[2 * k])[i] *
+               static_cast<const float*>(a.bufs[2 * k + 1])[block_of(a, i)];
     }
 };
 template <int DT>
 struct RawQuad {
     v2u w;
-    __device__ __forceinline__ void load(const void* p, int64_t i) {
-        w = ldnt_u2(static_cast<const uint16_t*>(p) + i);
+    __device__ __forceinline__ void load(const ReduceLaunch& a, int k, int64_t i, int64_t) {
+        w = ldnt_u2(static_cast<const uint16_t*>(a.bufs[k]) + i);
     }
     __device__ __forceinline__ void add_to(float acc[4]) const {
         acc[0] = acc[0] + cvt16<DT>(w.x & 0xffffu);
         acc[1] = acc[1] + cvt16<DT>(w.x >> 16);
         acc[2] = acc[2] + cvt16<DT>(w.y & 0xffffu);
         acc[3] = acc[3] + cvt16<DT>(w.y >> 16);
+    }
+    __device__ static __forceinline__ float one(const ReduceLaunch& a, int k, int64_t i) {
+        return cvt16<DT>(static_cast<const uint16_t*>(a.bufs[k])[i]);
     }
 };
 
@@ -308,14 +348,17 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
         auto load_group = [&](RawQuad<DT> (&x)[KC][TU], RawQuad<ZERO_F32> (&px)[TU], int64_t tt,
                               int gg) {
             const int64_t base = tt * kT + 4 * lane;
+            int64_t bi[TU];
+#pragma unroll
+            for (int j = 0; j < TU; ++j) bi[j] = DT == kQ8 ? block_of(a, base + 256 * j) : 0;
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk)
 #pragma unroll
-                for (int j = 0; j < TU; ++j) x[kk][j].load(a.bufs[gg * KC + kk], base + 256 * j);
+                for (int j = 0; j < TU; ++j) x[kk][j].load(a, gg * KC + kk, base + 256 * j, bi[j]);
             if constexpr (ACC) {
                 if (gg == 0) {
 #pragma unroll
-                    for (int j = 0; j < TU; ++j) px[j].load(a.red_out, base + 256 * j);
+                    for (int j = 0; j < TU; ++j) px[j].load_ptr(a.red_out, base + 256 * j);
                 }
             }
         };
@@ -376,7 +419,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int64_t i = base + 256 * j + c;
-                    if (i < n) acc[j][c] = acc[j][c] + load_one<DT>(a.bufs[k], i);
+                    if (i < n) acc[j][c] = acc[j][c] + RawQuad<DT>::one(a, k, i);
                 }
         }
         float prev[TU][4];
@@ -746,6 +789,13 @@ int launch_reduce_v(const ReduceLaunch& a, void* stream) {
     return a.vec ? launch_reduce_d<DT, true>(a, stream) : launch_reduce_d<DT, false>(a, stream);
 }
 
+// quantised payload: always writes the fp32 shard; statistics optional
+template <bool VEC>
+int launch_reduce_q8_v(const ReduceLaunch& a, void* stream) {
+    if (a.st) return launch_reduce_t<kQ8, VEC, true, true, false>(a, stream);
+    return launch_reduce_t<kQ8, VEC, true, false, false>(a, stream);
+}
+
 template <int GT, int PT, bool QUANT>
 int launch_adamw_q(const AdamLaunch& a, void* stream) {
     const int64_t ntiles = (a.n + kTile - 1) / kTile;
@@ -771,6 +821,10 @@ int launch_adamw_g(const AdamLaunch& a, void* stream) {
 }
 
 }  // namespace
+
+int launch_reduce_q8(const ReduceLaunch& a, void* stream) {
+    return a.vec ? launch_reduce_q8_v<true>(a, stream) : launch_reduce_q8_v<false>(a, stream);
+}
 
 int launch_reduce_stats(const ReduceLaunch& a, void* stream) {
     switch (a.dtype) {

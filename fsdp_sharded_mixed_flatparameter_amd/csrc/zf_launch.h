@@ -20,9 +20,14 @@ struct ReduceLaunch {
     int64_t n;
     float* red_out;  // may be null
     int32_t accumulate;     // 1: red_out += reduce (red_out is read, then written)
+    int32_t block;          // INT8 payload only: elements per scale
+    int32_t block_shift;    // log2(block) if a power of two, else -1
     zero_step_state_t* st;  // may be null
 };
 int launch_reduce_stats(const ReduceLaunch& a, void* stream);
+// The quantised-gradient reduce: bufs[2k] = rank k's INT8 codes, bufs[2k+1]
+// its fp32 block scales (n_ranks <= ZERO_MAX_RANKS / 2).
+int launch_reduce_q8(const ReduceLaunch& a, void* stream);
 
 struct AdamLaunch {
     const void* g;

@@ -6,7 +6,7 @@ arithmetic happens here; every part of the step runs in libzeroflat.
 import torch
 
 from . import (ZERO_AVG, StepState, zero_adamw_shard_step, zero_grad_accumulate_shard,
-               zero_grad_reduce_shard, zero_unscale_norm)
+               zero_grad_reduce_shard, zero_grad_reduce_shard_int8, zero_unscale_norm)
 
 
 class ShardOptimizer:
@@ -38,6 +38,17 @@ class ShardOptimizer:
         red = self.reduced_buffer()
         zero_grad_reduce_shard(grad_bufs, elem_offset, self.numel, op, red, self.state,
                                stream=stream)
+        self._apply(red, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
+                    q_scale_offset, stream)
+
+    def step_from_int8_grads(self, q_slices, scale_slices, allgather_buf, slot_offset,
+                             op=ZERO_AVG, block=256, q_buf=None, q_scales=None, q_slot_offset=0,
+                             q_scale_offset=0, stream=None):
+        """Reduce over the N ranks' INT8-quantised gradient slices for this rank
+        (ZeRO++'s quantised Reduce-Scatter), then the step."""
+        red = self.reduced_buffer()
+        zero_grad_reduce_shard_int8(q_slices, scale_slices, self.numel, op, red, self.state,
+                                    block=block, stream=stream)
         self._apply(red, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
                     q_scale_offset, stream)
 

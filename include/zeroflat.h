@@ -23,6 +23,8 @@
  *   6. zero_grad_accumulate_shard  gradient accumulation over micro-steps:
  *                              reduce as in 2, added into the rank's fp32
  *                              gradient shard.
+ *   7. zero_grad_reduce_shard_int8  the reduce of 2 over INT8-quantised rank
+ *                              gradients (blockwise codes + scales).
  *
  * Sources (three web pages, cited by title and section):
  *   "DeepSpeed 与 FSDP" (docs.ifdog.com): ZeRO-1/2/3 memory arithmetic,
@@ -313,6 +315,35 @@ int zero_dequant_allgather(const int8_t* q_buf, const float* q_scales, int32_t n
 int zero_grad_accumulate_shard(const void* const* grad_bufs, int32_t n_ranks, int32_t in_dtype,
                                int64_t elem_offset, int64_t shard_numel, int32_t op, float* acc,
                                zero_step_state_t* d_state, void* stream);
+/* ------------------------------------------------------------------------
+ * 7. Quantised gradient reduce.
+ *
+ * "DeepSpeed 与 FSDP", ZeRO++：量化通信压缩: gradients go through the
+ * Reduce-Scatter quantised (ZeRO++'s QG scheme), shrinking that collective
+ * by 2x or more.  The page fixes no scheme; the one used here is the
+ * parameter payload's (section 3): each rank sends its slice for this rank
+ * as INT8 codes with one fp32 scale per `block` elements, blocks restarting at
+ * the slice start, written by zero_quant_allgather_slot from its fp16/bf16
+ * gradient slice.  For i in [0, shard_numel):
+ *     acc = 0; for k = 0..n_ranks-1 (rank order):
+ *         acc += f32(q_bufs[k][i]) * scale_bufs[k][i / block]   (binary32 product, then add)
+ *     red_out[i] = (op == ZERO_AVG) ? acc / n_ranks : acc
+ * A block holding an inf is sent with scale inf, so its products here are NaN
+ * or inf and the fused statistics flag the overflow as in section 2.  A NaN
+ * alone does not survive quantisation (the quantiser codes it 0): the sending
+ * rank's own overflow test on its unquantised gradient has to report it, which
+ * reaches this rank through remote_overflow.
+ * q_bufs / scale_bufs: HOST arrays of n_ranks DEVICE pointers, already at this
+ *   rank's slice: int8[shard_numel] codes and fp32[ceil(shard_numel/block)]
+ *   scales (4-byte aligned).  1 <= n_ranks <= ZERO_MAX_RANKS/2; block a positive
+ *   multiple of 4.  red_out and d_state as in section 2.  The fast path needs
+ *   4-byte aligned code pointers and a 16-byte aligned red_out.  Reads
+ *   N*(1 + 4/block) bytes and writes 4 bytes per element (the fp16 reduce
+ *   reads 2N).
+ * ---------------------------------------------------------------------- */
+int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const* scale_bufs,
+                                int32_t n_ranks, int64_t shard_numel, int32_t block, int32_t op,
+                                float* red_out, zero_step_state_t* d_state, void* stream);
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,7 @@ class Workload:
     full_allgather: bool = True  # False: the slot is its own buffer (offset 0)
     inject: Optional[Tuple[int, int, int, float]] = None  # (step, rank buffer, flat index, value)
     micro_steps: int = 1       # > 1: gradient accumulation over this many micro-steps
+    grad_int8: bool = False    # rank gradients arrive INT8-quantised (blocks of 256)
     hp: dict = field(default_factory=lambda: dict(HP))
 
     @property
@@ -92,6 +93,14 @@ WORKLOADS = {
                                    steps=3, micro_steps=2),
     "10b_n8_accum2": Workload("10b_n8_accum2", (10_000_000_000,), 8, 7, F16, F16, True,
                               steps=5, micro_steps=2),
+    # quantised gradient Reduce-Scatter ("DeepSpeed 与 FSDP", ZeRO++): every rank's
+    # fp16 slice quantised to INT8 + block scales before the reduce
+    "tiny_mlp_n4_qg": Workload("tiny_mlp_n4_qg", TINY_MLP, 4, 2, F16, F16, True, steps=3,
+                               grad_int8=True),
+    "gpt1p5b_n64_qg": Workload("gpt1p5b_n64_qg", (1_500_000_000,), 64, 0, F16, F16, True,
+                               dynamic=True, steps=10, grad_int8=True),
+    "10b_n8_qg": Workload("10b_n8_qg", (10_000_000_000,), 8, 7, F16, F16, True, steps=5,
+                          grad_int8=True),
 }
 
 

@@ -179,3 +179,23 @@ def test_unflatten_views_follow_the_layout(zf):
         off += v.numel()
     with pytest.raises(ValueError):
         zf.unflatten(torch.zeros(10), shapes)
+
+
+def test_int8_gradient_reduce_validates_before_launch(zf):
+    L = zf.lib()
+    p = C.c_void_p(0x1000)
+    q = (C.c_void_p * 2)(0x1000, 0x2000)
+    s = (C.c_void_p * 2)(0x3000, 0x4000)
+    assert L.zero_grad_reduce_shard_int8(None, s, 2, 8, 256, 1, p, None, None) == -1
+    assert L.zero_grad_reduce_shard_int8(q, s, 0, 8, 256, 1, p, None, None) == -3
+    assert L.zero_grad_reduce_shard_int8(q, s, 129, 8, 256, 1, p, None, None) == -3
+    assert L.zero_grad_reduce_shard_int8(q, s, 2, 8, 256, 4, p, None, None) == -1
+    assert L.zero_grad_reduce_shard_int8(q, s, 2, 8, 250, 1, p, None, None) == -1
+    assert L.zero_grad_reduce_shard_int8(q, s, 2, -1, 256, 1, p, None, None) == -1
+    assert L.zero_grad_reduce_shard_int8(q, s, 2, 8, 256, 1, None, None, None) == -1
+    assert L.zero_grad_reduce_shard_int8(q, s, 2, 8, 256, 1, C.c_void_p(0x1002), None, None) == -2
+    bad = (C.c_void_p * 2)(0x3000, 0x4002)
+    assert L.zero_grad_reduce_shard_int8(q, bad, 2, 8, 256, 1, p, None, None) == -2
+    nul = (C.c_void_p * 2)(0x1000, 0)
+    assert L.zero_grad_reduce_shard_int8(nul, s, 2, 8, 256, 1, p, None, None) == -1
+    assert L.zero_grad_reduce_shard_int8(q, s, 2, 0, 256, 1, p, None, None) == 0
