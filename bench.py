@@ -14,8 +14,10 @@ is taken with HIP events on the launch stream around every launch.
 
 Also timed, each as whole steps: the other workloads (8- and 64-way reduces,
 the 70B INT8 shard, the 7B block, the Tiny MLP, gradient accumulation over 2
-micro-steps), and the INT8 All-Gather consumer (gathered slots dequantised into
-the full flat parameter) on the 7B block and the whole 70B flat parameter.
+micro-steps, INT8-quantised rank gradients), the ZeRO-Offload step (the
+update on host cores), and the INT8 All-Gather consumer (gathered slots
+dequantised into the full flat parameter) on the 7B block and the whole 70B
+flat parameter.
 
 Prints ONE JSON line.  --gpus N with N > 1 exits: the library runs one rank's
 step on one GPU.
@@ -322,6 +324,70 @@ def run_gather(zf, torch, g, steps, warmup):
             "bytes_per_param": need / g.padded, "GBps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS}
 
 
+def run_offload(zf, torch, w, steps, warmup):
+    """ZeRO-Offload on the same shard: statistics on the GPU, the fp16 gradient
+    to pinned host memory in chunks, the update on host cores over host-resident
+    fp32 master/m/v, the fp16 parameters back into the All-Gather slot.  Also
+    the host link's own rates (pinned 2.5 GB copies each way) and the host
+    threads' streaming rate, the two ceilings of this step."""
+    from synth import synth
+    from synth.workloads import key_grad_reduced, key_master
+    S = w.shard
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    master = torch.empty(S, dtype=torch.float32)
+    tmp = torch.empty(S, dtype=torch.float32, device="cuda")
+    synth.fill_normal(tmp, key_master(w), w.start, w.master_sigma)
+    master.copy_(tmp.cpu())
+    del tmp
+    opt = zf.OffloadShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic,
+                                   n_threads=threads)
+    g = torch.empty(S, dtype=torch.float16, device="cuda")
+    synth.fill_normal(g, key_grad_reduced(w, 0), w.start, w.grad_sigma)
+    ag = torch.zeros(w.padded, dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        opt.step_from_reduced(g, ag, w.start)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        opt.step_from_reduced(g, ag, w.start)
+    wall = (time.perf_counter() - t0) / steps
+    st = opt.state.read()
+    assert st.last_skipped == 0 and st.step == warmup + steps
+    # host link: pinned <-> device copies of the same 2.5 GB
+    stage = opt._staging(torch.float16)
+    rates = {}
+    for name, dst, src in (("d2h", stage, g), ("h2d", g, stage)):
+        best = 1e30
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.copy_(src, non_blocking=True)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        rates[name] = 2 * S / (best * 1e-3) / 1e9
+    # host memory: a threaded streaming copy of the master array
+    torch.set_num_threads(threads)
+    buf = torch.empty_like(master)
+    best = 1e30
+    for _ in range(3):
+        t1 = time.perf_counter()
+        buf.copy_(master)
+        best = min(best, time.perf_counter() - t1)
+    host_copy = 2 * 4 * S / best / 1e9
+    del opt, g, ag, master, buf, stage
+    torch.cuda.empty_cache()
+    host_bytes = 2 + 12 + 12 + 2                  # grad read, master/m/v read+write, fp16 write
+    return {"ms_per_step": wall * 1e3, "params_per_s": S / wall, "host_threads": threads,
+            "host_link_bytes_per_param": 4, "host_link_GBps": 4 * S / wall / 1e9,
+            "host_link_ceiling_GBps": rates, "host_bytes_per_param": host_bytes,
+            "host_GBps": host_bytes * S / wall / 1e9, "host_copy_ceiling_GBps": host_copy,
+            "what": "10B/8 rank-7 shard offloaded: fp32 state in host memory, AdamW on %d host "
+                    "threads, fp16 gradient down and fp16 parameters up over the host link"
+                    % threads}
+
+
 def run_copy_calibration(torch, nbytes=4 << 30, reps=3):
     from synth import synth
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -394,6 +460,7 @@ def main():
             r = run_workload(zf, torch, WORKLOADS[name], max(3, args.steps // 2), 2)
             r["what"] = what
             out["variants"][name] = r
+        out["offload"] = run_offload(zf, torch, w, 3, 1)
         from synth.workloads import GATHERS
         out["allgather_consumer"] = {}
         for name, what in GATHER_VARIANTS:

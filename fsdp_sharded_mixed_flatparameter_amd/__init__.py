@@ -23,7 +23,7 @@ ZERO_MAX_PARTIALS = 2048
 EXPORTS = ("zero_last_error", "zero_flat_layout", "zero_step_state_init",
            "zero_grad_reduce_shard", "zero_unscale_norm", "zero_adamw_shard_step",
            "zero_quant_allgather_slot", "zero_dequant_allgather", "zero_grad_accumulate_shard",
-           "zero_grad_reduce_shard_int8")
+           "zero_grad_reduce_shard_int8", "zero_offload_adamw_host", "zero_offload_step")
 
 
 class zero_span_t(C.Structure):
@@ -85,6 +85,11 @@ def _load():
     L.zero_grad_accumulate_shard.argtypes = [vp, i32, i32, i64, i64, i32, vp, vp, vp]
     L.zero_grad_reduce_shard_int8.restype = C.c_int
     L.zero_grad_reduce_shard_int8.argtypes = [vp, vp, i32, i64, i32, i32, vp, vp, vp]
+    L.zero_offload_adamw_host.restype = C.c_int
+    L.zero_offload_adamw_host.argtypes = [vp, i32, vp, vp, vp, i64, vp, i32, vp, vp, i32, vp]
+    L.zero_offload_step.restype = C.c_int
+    L.zero_offload_step.argtypes = [vp, i32, i64, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, i64,
+                                    i32, vp]
     return L
 
 
@@ -307,6 +312,62 @@ def zero_grad_reduce_shard_int8(q_slices, scale_slices, shard_numel, op, red_out
                                             _state_ptr(state), _stream(stream)))
 
 
+# ------------------------------------------------------------------ ZeRO-Offload
+def _host(t, name):
+    _contig(t, name)
+    if t.is_cuda:
+        raise ValueError("%s must be a host tensor" % name)
+    return t
+
+
+def zero_offload_adamw_host(grad, master, exp_avg, exp_avg_sq, lp_out, hp, host_state,
+                            n_threads=0):
+    """The AdamW step of one shard on host cores, over host tensors, with the
+    step scalars of `host_state` (a zero_step_state_t); returns 1 if the state
+    records an overflow (then nothing is written)."""
+    n = master.numel()
+    for name, t in (("grad", grad), ("master", master), ("exp_avg", exp_avg),
+                    ("exp_avg_sq", exp_avg_sq), ("lp_out", lp_out)):
+        _host(t, name)
+    if grad.numel() < n or exp_avg.numel() != n or exp_avg_sq.numel() != n or lp_out.numel() < n:
+        raise ValueError("host tensors disagree in size")
+    h = hp if isinstance(hp, zero_adamw_hparams_t) else zero_adamw_hparams_t(**hp)
+    sk = C.c_int32(0)
+    _check(_lib.zero_offload_adamw_host(_ptr(grad), _dtype_code(grad), _ptr(master), _ptr(exp_avg),
+                                        _ptr(exp_avg_sq), n, _ptr(lp_out), _dtype_code(lp_out),
+                                        C.byref(h), C.byref(host_state), n_threads, C.byref(sk)))
+    return sk.value
+
+
+def zero_offload_step(grad_shard, master, exp_avg, exp_avg_sq, grad_stage, lp_stage,
+                      allgather_buf, slot_offset, hp, state, chunk=0, n_threads=0, stream=None):
+    """ZeRO-Offload step: the device gradient shard to pinned host staging in
+    chunks, the update on host cores over host master/m/v, the 16-bit
+    parameters back into allgather_buf[slot_offset:], then the device
+    loss-scaler update.  Blocks until done."""
+    n = master.numel()
+    _contig(grad_shard, "grad_shard")
+    _contig(allgather_buf, "allgather_buf")
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq),
+                    ("grad_stage", grad_stage), ("lp_stage", lp_stage)):
+        _host(t, name)
+    if not grad_stage.is_pinned() or not lp_stage.is_pinned():
+        raise ValueError("the staging buffers must be pinned host memory")
+    if grad_shard.numel() < n or grad_stage.numel() < n or lp_stage.numel() < n or \
+            exp_avg.numel() != n or exp_avg_sq.numel() != n:
+        raise ValueError("tensors disagree in size")
+    if grad_stage.dtype != grad_shard.dtype or lp_stage.dtype != allgather_buf.dtype:
+        raise ValueError("staging dtypes must match the device tensors")
+    if slot_offset + n > allgather_buf.numel():
+        raise ValueError("slot exceeds the all-gather buffer")
+    h = hp if isinstance(hp, zero_adamw_hparams_t) else zero_adamw_hparams_t(**hp)
+    _check(_lib.zero_offload_step(_ptr(grad_shard), _dtype_code(grad_shard), n, _ptr(master),
+                                  _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad_stage),
+                                  _ptr(lp_stage), _ptr(allgather_buf), _dtype_code(allgather_buf),
+                                  slot_offset, C.byref(h), _state_ptr(state), chunk, n_threads,
+                                  _stream(stream)))
+
+
 # ------------------------------------------------------------------ All-Gather consumer
 def zero_dequant_allgather(q_buf, q_scales, n_slots, slot_numel, out, block=256, stream=None):
     """out[s*S + i] = round(f32(q) * scale) over the n_slots gathered INT8 slots
@@ -336,4 +397,4 @@ def unflatten(flat, shapes, n_ranks=1, align=1):
 
 
 from . import shard  # noqa: E402
-from .shard import ShardOptimizer  # noqa: E402,F401
+from .shard import OffloadShardOptimizer, ShardOptimizer  # noqa: E402,F401

@@ -367,6 +367,83 @@ int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const*
 }
 
 // ---------------------------------------------------------------------------
+// ZeRO-Offload ("DeepSpeed 与 FSDP", ZeRO-Offload; 2kiu.com §4.1, §5.1).
+namespace {
+int check_hp(const char* fn, const zero_adamw_hparams_t* hp) {
+    if (!hp) return fail(ZERO_EINVAL, "%s: NULL hp", fn);
+    if (!(hp->lr >= 0.0) || !(hp->eps > 0.0) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
+        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->weight_decay >= 0.0))
+        return fail(ZERO_EINVAL, "%s: hyper-parameters out of range", fn);
+    return ZERO_OK;
+}
+}  // namespace
+
+int zero_offload_adamw_host(const void* grad, int32_t grad_dtype, float* master, float* exp_avg,
+                            float* exp_avg_sq, int64_t n, void* lp_out, int32_t param_dtype,
+                            const zero_adamw_hparams_t* hp, const zero_step_state_t* host_state,
+                            int32_t n_threads, int32_t* skipped) {
+    const char* fn = "zero_offload_adamw_host";
+    if (int e = check_hp(fn, hp)) return e;
+    if (!host_state || !skipped) return fail(ZERO_EINVAL, "%s: NULL state or skipped", fn);
+    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "%s: bad grad_dtype %d", fn, grad_dtype);
+    if (param_dtype != ZERO_F16 && param_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "%s: param_dtype must be fp16 or bf16", fn);
+    if (n < 0 || n_threads < 0) return fail(ZERO_EINVAL, "%s: negative size or thread count", fn);
+    if (n > 0 && (!grad || !master || !exp_avg || !exp_avg_sq || !lp_out))
+        return fail(ZERO_EINVAL, "%s: NULL array", fn);
+    if (n > 0 && (!aligned(grad, esize(grad_dtype)) || !aligned(master, 4) || !aligned(exp_avg, 4) ||
+                  !aligned(exp_avg_sq, 4) || !aligned(lp_out, 2)))
+        return fail(ZERO_EALIGN, "%s: an array is not aligned to its element size", fn);
+    int sk = 0;
+    zf::offload_adam_host(grad, grad_dtype, master, exp_avg, exp_avg_sq, n, lp_out, param_dtype, *hp,
+                          *host_state, n_threads, &sk);
+    *skipped = sk;
+    return ok();
+}
+
+int zero_offload_step(const void* d_grad, int32_t grad_dtype, int64_t n, float* h_master,
+                      float* h_exp_avg, float* h_exp_avg_sq, void* h_grad_stage, void* h_lp_stage,
+                      void* d_allgather, int32_t param_dtype, int64_t slot_offset,
+                      const zero_adamw_hparams_t* hp, zero_step_state_t* d_state, int64_t chunk,
+                      int32_t n_threads, void* stream) {
+    const char* fn = "zero_offload_step";
+    if (int e = check_hp(fn, hp)) return e;
+    if (!d_state) return fail(ZERO_EINVAL, "%s: NULL state", fn);
+    if (!aligned(d_state, 8)) return fail(ZERO_EALIGN, "%s: state not 8-byte aligned", fn);
+    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "%s: bad grad_dtype %d", fn, grad_dtype);
+    if (param_dtype != ZERO_F16 && param_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "%s: param_dtype must be fp16 or bf16", fn);
+    if (n < 0 || slot_offset < 0 || chunk < 0 || n_threads < 0)
+        return fail(ZERO_EINVAL, "%s: negative size, offset, chunk or thread count", fn);
+    if (n > 0 && (!d_grad || !h_master || !h_exp_avg || !h_exp_avg_sq || !h_grad_stage ||
+                  !h_lp_stage || !d_allgather))
+        return fail(ZERO_EINVAL, "%s: NULL pointer", fn);
+    const int es = esize(grad_dtype);
+    if (n > 0 && (!aligned(d_grad, es) || !aligned(h_grad_stage, es) || !aligned(h_master, 4) ||
+                  !aligned(h_exp_avg, 4) || !aligned(h_exp_avg_sq, 4) || !aligned(h_lp_stage, 2) ||
+                  !aligned(d_allgather, 2)))
+        return fail(ZERO_EALIGN, "%s: a buffer is not aligned to its element size", fn);
+    zf::OffloadLaunch a;
+    memset(&a, 0, sizeof a);
+    a.d_grad = d_grad;
+    a.gdtype = grad_dtype;
+    a.pdtype = param_dtype;
+    a.n = n;
+    a.h_p = h_master;
+    a.h_m = h_exp_avg;
+    a.h_v = h_exp_avg_sq;
+    a.h_grad = h_grad_stage;
+    a.h_lp = h_lp_stage;
+    a.d_slot = n > 0 ? static_cast<uint16_t*>(d_allgather) + slot_offset : nullptr;
+    a.chunk = chunk > 0 ? chunk : (int64_t)1 << 24;
+    a.n_threads = n_threads;
+    a.st = d_state;
+    const int e = zf::offload_step(a, *hp, stream);
+    if (e) return hip_fail(e, fn);
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
 // INT8 All-Gather consumer ("DeepSpeed 与 FSDP", ZeRO++：量化通信压缩;
 // 2kiu.com §4.2): the gathered slots back to the flat parameter.
 int zero_dequant_allgather(const int8_t* q_buf, const float* q_scales, int32_t n_slots,

@@ -71,6 +71,31 @@ struct DequantLaunch {
 };
 int launch_dequant(const DequantLaunch& a, void* stream);
 
+// ZeRO-Offload (zeroflat_offload.cpp).  The host update over host arrays:
+// *skipped = 1 (and nothing written) when the state says overflow.
+int offload_adam_host(const void* g, int32_t gdt, float* p, float* m, float* v, int64_t n,
+                      void* lp, int32_t pdt, const zero_adamw_hparams_t& hp,
+                      const zero_step_state_t& st, int32_t n_threads, int* skipped);
+// The pipelined step: gradient chunks device->host, host update, 16-bit
+// parameter chunks host->device into the slot, then the device finalize.
+// Blocks the calling thread until every copy has completed.
+struct OffloadLaunch {
+    const void* d_grad;
+    int32_t gdtype;
+    int32_t pdtype;
+    int64_t n;
+    float* h_p;
+    float* h_m;
+    float* h_v;
+    void* h_grad;     // pinned staging, n gradient elements
+    void* h_lp;       // pinned staging, n 16-bit parameters
+    void* d_slot;     // the All-Gather slot, already offset
+    int64_t chunk;
+    int32_t n_threads;
+    zero_step_state_t* st;
+};
+int offload_step(const OffloadLaunch& a, const zero_adamw_hparams_t& hp, void* stream);
+
 const char* hip_error_string(int err);
 
 }  // namespace zf

@@ -6,7 +6,8 @@ arithmetic happens here; every part of the step runs in libzeroflat.
 import torch
 
 from . import (ZERO_AVG, StepState, zero_adamw_shard_step, zero_grad_accumulate_shard,
-               zero_grad_reduce_shard, zero_grad_reduce_shard_int8, zero_unscale_norm)
+               zero_grad_reduce_shard, zero_grad_reduce_shard_int8, zero_offload_step,
+               zero_unscale_norm)
 
 
 class ShardOptimizer:
@@ -86,3 +87,41 @@ class ShardOptimizer:
                               slot_offset, self.hp, self.state, q_buf=q_buf, q_scales=q_scales,
                               q_slot_offset=q_slot_offset, q_scale_offset=q_scale_offset,
                               q_block=self.quant_block or 256, finalize=True, stream=stream)
+
+
+class OffloadShardOptimizer:
+    """ZeRO-Offload for one rank's shard: the fp32 master, m and v live in host
+    memory and the update runs on host cores; the device keeps the gradient
+    shard, the step state and the All-Gather buffer.  Pinned staging buffers
+    carry the gradient to the host and the 16-bit parameters back."""
+
+    def __init__(self, master_host, hp, loss_scale=65536.0, dynamic=False, window=1000,
+                 min_scale=1.0, device="cuda", n_threads=0, chunk=0):
+        if master_host.dtype != torch.float32 or master_host.is_cuda or \
+                not master_host.is_contiguous():
+            raise ValueError("master must be a contiguous float32 host tensor")
+        self.master = master_host
+        self.exp_avg = torch.zeros_like(master_host)
+        self.exp_avg_sq = torch.zeros_like(master_host)
+        self.hp = dict(hp)
+        self.state = StepState(loss_scale, dynamic, window, min_scale, device=device)
+        self.n_threads = n_threads
+        self.chunk = chunk
+        self._stage = {}
+
+    @property
+    def numel(self):
+        return self.master.numel()
+
+    def _staging(self, dtype):
+        if dtype not in self._stage:
+            self._stage[dtype] = torch.empty(self.numel, dtype=dtype, pin_memory=True)
+        return self._stage[dtype]
+
+    def step_from_reduced(self, grad_shard, allgather_buf, slot_offset, stream=None):
+        """Statistics over the device gradient shard, then the offloaded step."""
+        zero_unscale_norm(grad_shard, self.state, n=self.numel, stream=stream)
+        zero_offload_step(grad_shard, self.master, self.exp_avg, self.exp_avg_sq,
+                          self._staging(grad_shard.dtype), self._staging(allgather_buf.dtype),
+                          allgather_buf, slot_offset, self.hp, self.state, chunk=self.chunk,
+                          n_threads=self.n_threads, stream=stream)

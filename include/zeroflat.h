@@ -25,6 +25,9 @@
  *                              gradient shard.
  *   7. zero_grad_reduce_shard_int8  the reduce of 2 over INT8-quantised rank
  *                              gradients (blockwise codes + scales).
+ *   8. zero_offload_adamw_host / zero_offload_step  ZeRO-Offload: the step of
+ *                              3 on host cores over host-resident fp32 state,
+ *                              with the transfers pipelined around it.
  *
  * Sources (three web pages, cited by title and section):
  *   "DeepSpeed 与 FSDP" (docs.ifdog.com): ZeRO-1/2/3 memory arithmetic,
@@ -344,6 +347,46 @@ int zero_grad_accumulate_shard(const void* const* grad_bufs, int32_t n_ranks, in
 int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const* scale_bufs,
                                 int32_t n_ranks, int64_t shard_numel, int32_t block, int32_t op,
                                 float* red_out, zero_step_state_t* d_state, void* stream);
+/* ------------------------------------------------------------------------
+ * 8. ZeRO-Offload: the optimizer step on host cores.
+ *
+ * "DeepSpeed 与 FSDP", ZeRO-Offload: the fp32 optimizer state (master, m, v)
+ * lives in CPU memory and the Adam update runs on the CPU; fp16 gradients go
+ * to the host and the updated fp16 parameters come back.  2kiu.com §4.1
+ * (states moved to CPU memory) and §5.1 (offload_optimizer: cpu, pin_memory).
+ * The update is section 3's, computed in the same binary32 order, so it is
+ * bit-identical to the GPU step; the skip, clip and bias-correction scalars
+ * come from the step state exactly as on the device.
+ *
+ * zero_offload_adamw_host: HOST arrays only (grad[n] of grad_dtype, master,
+ *   exp_avg, exp_avg_sq fp32[n], lp_out[n] of param_dtype); host_state is a
+ *   HOST copy of the step state after the statistics calls; nothing is
+ *   written and *skipped = 1 if it records an overflow.  It does not update
+ *   the loss scaler (see below).  n_threads host threads (0: every hardware
+ *   thread).  Blocks until done; no HIP calls.
+ * zero_offload_step: the whole offloaded step for a rank whose statistics
+ *   (zero_grad_reduce_shard / zero_unscale_norm into d_state) are already
+ *   enqueued on `stream`.  The DEVICE gradient shard d_grad[n] moves to the
+ *   PINNED host staging buffer h_grad_stage (n elements of grad_dtype) in
+ *   chunks of `chunk` elements on `stream`; each chunk is updated on the host
+ *   as soon as it has landed (HOST h_master/h_exp_avg/h_exp_avg_sq fp32[n]),
+ *   its 16-bit parameters go to the PINNED h_lp_stage[n] and from there to the
+ *   DEVICE All-Gather slot d_allgather[slot_offset ...] while later chunks are
+ *   computed; finally the loss scaler / counters of d_state are updated on the
+ *   device as by ZERO_STEP_FINALIZE.  Unlike the sections above this call
+ *   synchronizes: it returns after every copy and the finalize completed.  It
+ *   creates and destroys its own HIP events and host threads, and allocates no
+ *   device memory.  chunk 0 selects 2^24 elements.
+ * ---------------------------------------------------------------------- */
+int zero_offload_adamw_host(const void* grad, int32_t grad_dtype, float* master, float* exp_avg,
+                            float* exp_avg_sq, int64_t n, void* lp_out, int32_t param_dtype,
+                            const zero_adamw_hparams_t* hp, const zero_step_state_t* host_state,
+                            int32_t n_threads, int32_t* skipped);
+int zero_offload_step(const void* d_grad, int32_t grad_dtype, int64_t n, float* h_master,
+                      float* h_exp_avg, float* h_exp_avg_sq, void* h_grad_stage, void* h_lp_stage,
+                      void* d_allgather, int32_t param_dtype, int64_t slot_offset,
+                      const zero_adamw_hparams_t* hp, zero_step_state_t* d_state, int64_t chunk,
+                      int32_t n_threads, void* stream);
 #ifdef __cplusplus
 }
 #endif
