@@ -353,8 +353,17 @@ def run_offload(zf, torch, w, steps, warmup):
     wall = (time.perf_counter() - t0) / steps
     st = opt.state.read()
     assert st.last_skipped == 0 and st.step == warmup + steps
-    # host link: pinned <-> device copies of the same 2.5 GB
+    # the host update alone (no copies), same threads, same arrays
     stage = opt._staging(torch.float16)
+    lp_out = torch.empty(S, dtype=torch.float16)
+    best = 1e30
+    for _ in range(2):
+        t1 = time.perf_counter()
+        zf.zero_offload_adamw_host(stage, opt.master, opt.exp_avg, opt.exp_avg_sq, lp_out, w.hp,
+                                   st, threads)
+        best = min(best, time.perf_counter() - t1)
+    host_only = best
+    # host link: pinned <-> device copies of the same 2.5 GB
     rates = {}
     for name, dst, src in (("d2h", stage, g), ("h2d", g, stage)):
         best = 1e30
@@ -376,13 +385,15 @@ def run_offload(zf, torch, w, steps, warmup):
         buf.copy_(master)
         best = min(best, time.perf_counter() - t1)
     host_copy = 2 * 4 * S / best / 1e9
-    del opt, g, ag, master, buf, stage
+    del opt, g, ag, master, buf, stage, lp_out
     torch.cuda.empty_cache()
     host_bytes = 2 + 12 + 12 + 2                  # grad read, master/m/v read+write, fp16 write
     return {"ms_per_step": wall * 1e3, "params_per_s": S / wall, "host_threads": threads,
             "host_link_bytes_per_param": 4, "host_link_GBps": 4 * S / wall / 1e9,
             "host_link_ceiling_GBps": rates, "host_bytes_per_param": host_bytes,
             "host_GBps": host_bytes * S / wall / 1e9, "host_copy_ceiling_GBps": host_copy,
+            "host_update_only_ms": host_only * 1e3,
+            "host_update_only_GBps": host_bytes * S / host_only / 1e9,
             "what": "10B/8 rank-7 shard offloaded: fp32 state in host memory, AdamW on %d host "
                     "threads, fp16 gradient down and fp16 parameters up over the host link"
                     % threads}

@@ -261,6 +261,10 @@ int offload_step(const OffloadLaunch& a, const zero_adamw_hparams_t& hp, void* s
     if (e == hipSuccess) e = hipEventSynchronize(ev_state);  // the state only
     Scalars s;
     const int skipped = e == hipSuccess && !step_scalars(st, hp, &s);
+    // parameters go up on a stream of their own (default priority), so that the
+    // link carries both directions at once
+    hipStream_t up = nullptr;
+    if (e == hipSuccess && !skipped && a.n > 0) e = hipStreamCreateWithFlags(&up, hipStreamNonBlocking);
     if (e == hipSuccess && !skipped && a.n > 0) {
         Pool pool(std::min<int64_t>(threads_for(a.n_threads), std::max<int64_t>(1, a.chunk / 4096)));
         uint16_t* lp = static_cast<uint16_t*>(a.h_lp);
@@ -273,8 +277,13 @@ int offload_step(const OffloadLaunch& a, const zero_adamw_hparams_t& hp, void* s
             if (e != hipSuccess) break;
             pool.run(lo, lo + len, fn);
             e = hipMemcpyAsync(static_cast<uint16_t*>(a.d_slot) + lo, lp + lo, len * 2,
-                               hipMemcpyHostToDevice, stream);
+                               hipMemcpyHostToDevice, up);
         }
+    }
+    if (up) {
+        const hipError_t e2 = hipStreamSynchronize(up);
+        if (e == hipSuccess) e = e2;
+        (void)hipStreamDestroy(up);
     }
     if (e != hipSuccess) (void)hipStreamSynchronize(stream);  // no copy may outlive the call
     for (auto x : ev)
