@@ -162,6 +162,7 @@ int reduce_entry(const char* fn, const void* const* grad_bufs, int32_t n_ranks, 
     if (op != ZERO_SUM && op != ZERO_AVG) return fail(ZERO_EINVAL, "%s: bad op %d", fn, op);
     if (elem_offset < 0 || shard_numel < 0)
         return fail(ZERO_EINVAL, "%s: negative offset or size", fn);
+    if (shard_numel == 0) return ok();  // nothing is read or written
     if (!red_out) return fail(ZERO_EINVAL, "%s: output shard is NULL", fn);
     if (!aligned(red_out, 4)) return fail(ZERO_EALIGN, "%s: output shard not 4-byte aligned", fn);
     if (d_state && !aligned(d_state, 8)) return fail(ZERO_EALIGN, "%s: state not 8-byte aligned", fn);
@@ -179,7 +180,6 @@ int reduce_entry(const char* fn, const void* const* grad_bufs, int32_t n_ranks, 
         a.bufs[k] = p;
         vec = vec && aligned(p, 4 * es);
     }
-    if (shard_numel == 0) return ok();
     a.n_ranks = n_ranks;
     a.dtype = in_dtype;
     a.op = op;
@@ -213,9 +213,11 @@ int zero_grad_accumulate_shard(const void* const* grad_bufs, int32_t n_ranks, in
 
 int zero_unscale_norm(const void* grad_shard, int32_t dtype, int64_t n, zero_step_state_t* d_state,
                       void* stream) {
-    if (!grad_shard || !d_state) return fail(ZERO_EINVAL, "zero_unscale_norm: NULL pointer");
+    if (!d_state) return fail(ZERO_EINVAL, "zero_unscale_norm: NULL state");
     if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "zero_unscale_norm: bad dtype %d", dtype);
     if (n < 0) return fail(ZERO_EINVAL, "zero_unscale_norm: n < 0");
+    if (n == 0) return ok();  // nothing is read
+    if (!grad_shard) return fail(ZERO_EINVAL, "zero_unscale_norm: grad_shard is NULL");
     if (!aligned(grad_shard, esize(dtype))) return fail(ZERO_EALIGN, "zero_unscale_norm: grad misaligned");
     if (!aligned(d_state, 8)) return fail(ZERO_EALIGN, "zero_unscale_norm: state not 8-byte aligned");
     if (n == 0) return ok();
@@ -338,6 +340,7 @@ int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const*
     if (op != ZERO_SUM && op != ZERO_AVG) return fail(ZERO_EINVAL, "%s: bad op %d", fn, op);
     if (shard_numel < 0) return fail(ZERO_EINVAL, "%s: negative size", fn);
     if (block < 4 || block % 4 != 0) return fail(ZERO_EINVAL, "%s: block %d is not a positive multiple of 4", fn, block);
+    if (shard_numel == 0) return ok();  // nothing is read or written
     if (!red_out) return fail(ZERO_EINVAL, "%s: red_out is NULL", fn);
     if (!aligned(red_out, 4)) return fail(ZERO_EALIGN, "%s: red_out not 4-byte aligned", fn);
     if (d_state && !aligned(d_state, 8)) return fail(ZERO_EALIGN, "%s: state not 8-byte aligned", fn);
@@ -351,7 +354,6 @@ int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const*
         a.bufs[2 * k + 1] = scale_bufs[k];
         vec = vec && aligned(q_bufs[k], 4);
     }
-    if (shard_numel == 0) return ok();
     a.n_ranks = n_ranks;
     a.dtype = ZERO_F32;  // unused by the INT8 source
     a.op = op;

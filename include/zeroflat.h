@@ -50,6 +50,10 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); all
  *     kernels of a call are enqueued on it, in order.
  *   - Element counts and offsets are int64 (slot offsets exceed 2^31).
+ *   - A call over zero elements reads and writes nothing, and the pointers it
+ *     would have used may be NULL (empty tensors); the step state is still
+ *     required where the call updates it (a finalize on an empty shard still
+ *     advances the counters).
  *   - One zero_step_state_t must not be used by two streams at once.
  */
 #ifndef ZEROFLAT_H
