@@ -1,5 +1,15 @@
 // zeroflat_kernels.hip -- gfx950 (MI355X, CDNA4, wave64) kernels of one
-// rank's sharded mixed-precision AdamW step over a FlatParameter.
+// rank's sharded mixed-precision AdamW step over a FlatParameter:
+//   reduce_kernel    N-way reduce of the rank buffers (fp32/fp16/bf16, or INT8
+//                    codes with block scales), optionally added into the fp32
+//                    shard (gradient accumulation), fused with the step
+//                    statistics; with one buffer and no output, the statistics
+//                    pass of a pre-reduced shard
+//   fold_kernel      the statistics' per-block partial sums, in a fixed order
+//   adamw_kernel     skip/clip prologue, fused AdamW, 16-bit write-back, INT8
+//   finalize_kernel  loss scaler and counters
+//   quant_kernel     INT8 of an existing 16-bit slot
+//   dequant_kernel   the INT8 All-Gather consumer
 //
 // Every kernel here streams HBM once: none is a contraction, so there is no
 // MFMA work; the design goals are wide coalesced accesses, enough bytes in
@@ -203,9 +213,12 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // that leaves half of each cache line to another instruction costs about a
 // third of the bandwidth here.
 //
-// Work split: each wave owns one contiguous run of tiles.  Striding the grid
-// over the array instead (every wave in the same narrow window at a time)
-// measured about 20% slower on this part for the 8-buffer reduce.
+// Work split: the grid is persistent (one partial per block), and wave w
+// walks runs of R consecutive tiles: run w, then run w + nwaves, ...  So the
+// waves resident at one time work in one window of the arrays.  Measured on
+// the 10B/8 shard: R = 2 beats one contiguous run per wave by 5% (8 fp16
+// buffers) to 7% (64 buffers); the INT8 source, with its scale loads, does best
+// at R = 16 (+6%).
 //
 // Pipelining: a wave walks (tile, group of KC buffers) pairs in order and
 // issues the reads of the next pair before adding the current one and before
@@ -280,7 +293,7 @@ struct RawQuad {
 
 template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float inv_n,
-                                                          int pow2_n) {
+                                                          int pow2_n, int run_tiles) {
     static_assert(WRITE || !ACC, "accumulation writes its output");
     constexpr int64_t kT = 256 * TU;
     const int lane = threadIdx.x & 63;
@@ -339,10 +352,10 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
     const int64_t ntiles = (n + kT - 1) / kT;
     const int64_t nfull = VEC ? n / kT : 0;
     // ---- full tiles: wave w owns tiles [w*per, min((w+1)*per, nfull))
-    const int64_t per = (nfull + nwaves - 1) / nwaves;
-    const int64_t t_begin = wave_id * per;
-    const int64_t t_end = t_begin + per < nfull ? t_begin + per : nfull;
-    if (t_begin < t_end) {
+    // Wave w walks runs of R consecutive tiles: run w, then run w + nwaves, ...
+    const int64_t R = run_tiles;
+    const int64_t t_begin = wave_id * R;
+    if (t_begin < nfull) {
         RawQuad<DT> cur[KC][TU], nxt[KC][TU];
         RawQuad<ZERO_F32> pcur[TU], pnxt[TU];   // accumulator quads (ACC only)
         auto load_group = [&](RawQuad<DT> (&x)[KC][TU], RawQuad<ZERO_F32> (&px)[TU], int64_t tt,
@@ -364,6 +377,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
         };
         load_group(cur, pcur, t_begin, 0);
         int64_t t = t_begin;
+        int64_t left = R;  // tiles of the current run still to finish, t included
         int g = 0;
         float acc[TU][4];
 #pragma unroll
@@ -375,8 +389,11 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
             // pair (harmless, in bounds, never used)
             int gn = g + 1;
             int64_t tn = t;
-            if (gn == ngroups) { gn = 0; tn = t + 1; }
-            const bool more = tn < t_end;
+            if (gn == ngroups) {
+                gn = 0;
+                tn = left == 1 ? t + 1 + (nwaves - 1) * R : t + 1;
+            }
+            const bool more = tn < nfull;
             load_group(nxt, pnxt, more ? tn : t, more ? gn : g);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -401,6 +418,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
             if constexpr (ACC) {
                 if (gn == 0) __builtin_memcpy(pcur, pnxt, sizeof(pcur));
             }
+            if (gn == 0) left = left == 1 ? R : left - 1;
             t = tn;
             g = gn;
         }
@@ -748,8 +766,9 @@ void launch_reduce_shape(const ReduceLaunch& a, void* stream, float inv_n, int p
     int grid = grid_for_tiles(ntiles, kMaxGridReduce);
     const int round = resident_blocks(kernel);
     if (round > 0 && grid > round) grid = (grid / round) * round;
+    const int run = DT == kQ8 ? 16 : 2;  // tiles per run (see reduce_kernel)
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, a, inv_n,
-                       pow2);
+                       pow2, run);
 }
 
 template <int DT, bool VEC, bool WRITE, bool STATS, bool ACC>
