@@ -612,7 +612,9 @@ __global__ void finalize_kernel(zero_step_state_t* st, double beta1, double beta
         if (st->dynamic) {
             st->good_steps = st->good_steps + 1;
             if (st->good_steps == st->window) {
-                st->loss_scale = st->loss_scale * 2.0f;
+                // doubling stops at 2^127 (the largest binary32 power of two), so
+                // the scale and its reciprocal stay finite and exact
+                if (st->loss_scale < 0x1p127f) st->loss_scale = st->loss_scale * 2.0f;
                 st->good_steps = 0;
             }
         }

@@ -232,7 +232,8 @@ int zero_unscale_norm(const void* grad_shard, int32_t dtype, int64_t n,
  *   if (flags & ZERO_STEP_FINALIZE): loss scaler and counters -- on overflow
  *     scale = max(scale/2, min_scale) if dynamic, good_steps = 0; else
  *     step += 1, beta pows *= betas, and if dynamic good_steps += 1 with the
- *     scale doubled (good_steps = 0) when good_steps reaches window; then
+ *     scale doubled (not past 2^127) and good_steps = 0 when good_steps
+ *     reaches window; then
  *     sumsq = 0 and overflow = 0 for the next step, last_* filled in.
  *     Pass it on the last (or only) FlatParameter of the optimizer step.
  *

@@ -397,7 +397,8 @@ void oracle_scaler_update(oracle_scaler* s, int32_t overflow) {
     if (s->dynamic) {
         s->good_steps += 1;
         if (s->good_steps == s->window) {
-            s->loss_scale = s->loss_scale * 2.0f;
+            /* doubling stops at 2^127, the largest binary32 power of two */
+            if (s->loss_scale < 0x1p127f) s->loss_scale = s->loss_scale * 2.0f;
             s->good_steps = 0;
         }
     }

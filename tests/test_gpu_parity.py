@@ -412,3 +412,19 @@ def test_writeback_rounding_exhaustive_cases(zf, pdt):
     nan = np.isnan(x)
     assert_bitwise(got[~nan], ref[~nan], "write-back rounding")
     assert_bitwise(got[nan], ref[nan], "NaN write-back")
+
+
+def test_loss_scale_stops_doubling_at_2_pow_127(zf):
+    """Finalizes on an empty shard with window 1 from 2^126: the scale reaches
+    2^127 and stays there (the oracle's scaler does the same)."""
+    state = zf.StepState(2.0 ** 126, True, window=1)
+    ref = orc.make_scaler(2.0 ** 126, True, window=1)
+    empty = torch.zeros(0, device="cuda")
+    g = torch.zeros(0, dtype=torch.float16, device="cuda")
+    ag = torch.zeros(1, dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        zf.zero_adamw_shard_step(g, empty, empty, empty, ag, 0, HP, state, finalize=True)
+        orc.scaler_update(ref, 0)
+        st = state.read()
+        assert (st.loss_scale, st.good_steps, st.step) == (ref.loss_scale, ref.good_steps, ref.step)
+    assert st.loss_scale == 2.0 ** 127

@@ -56,6 +56,8 @@ MUTANTS = [
     ("norm_fp32_square", "s = s + (double)u * (double)u;", "s = s + (double)(u * u);", STEP),
     ("clip_without_epsilon", "const double c = max_norm / (std::sqrt(sumsq_total) + 1e-6);",
      "const double c = max_norm / std::sqrt(sumsq_total);", STEP),
+    ("scaler_grows_to_inf", "if (s->loss_scale < 0x1p127f) s->loss_scale",
+     "if (1) s->loss_scale", STEP),
     ("scaler_grows_late", "if (s->good_steps == s->window) {",
      "if (s->good_steps == s->window + 1) {", STEP),
     ("scaler_static_halves", "if (s->dynamic) {\n            const float h",

@@ -351,6 +351,13 @@ def test_scaler_sequence(orc):
     assert w1000.loss_scale == 2.0 ** 16
     orc.scaler_update(w1000, 0)
     assert w1000.loss_scale == 2.0 ** 17 and w1000.step == 1000
+    # the scale stays a finite power of two: doubling stops at 2^127
+    top = orc.make_scaler(2.0 ** 126, True, window=1)
+    for _ in range(3):
+        orc.scaler_update(top, 0)
+    assert top.loss_scale == 2.0 ** 127 and top.step == 3
+    orc.scaler_update(top, 1)
+    assert top.loss_scale == 2.0 ** 126
 
 
 # ------------------------------------------------------------------ INT8
