@@ -474,22 +474,49 @@ __global__ void __launch_bounds__(kThreads) fold_kernel(zero_step_state_t* st) {
 // ---------------------------------------------------------------- INT8 of one slice
 // x[4]: this lane's four written values (zero for elements past the end).
 // One 256-element block per wave slice: amax across the wave, then codes.
+//
+// The code is rint(x / scale) with the IEEE quotient, whose division sequence
+// dominates this function.  The quotient is first taken as y = x * (1/scale)
+// (two roundings): that is within |q| * 2^-22 of the IEEE quotient q, and
+// |q| <= 127.0002 here (|x| <= amax, scale = amax/127 rounded), so within
+// 2^-15, and both round to the same integer unless y lies within 2^-15 of a
+// half-integer.  Elements within 2^-14 of one (about one in 8000) take the
+// exact division, in a branch the whole wave skips when no lane needs it; so
+// does every element when 1/scale is infinite or zero (scale below 2^-128, or
+// infinite).
 __device__ __forceinline__ uint32_t quant_quad(const float x[4], float* scale_out) {
     float a = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) a = fmaxf(a, fabsf(x[c]));
     const float amax = wave_max(a);
     const float scale = amax / 127.0f;
+    const float rs = 1.0f / scale;
+    const bool fast = isfinite(rs) && rs != 0.0f;
+    float r[4];
+    bool exact[4];
+    bool any = false;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float y = x[c] * rs;
+        const float f = y - floorf(y);                  // the fraction, within 2^-24
+        exact[c] = !fast || fabsf(f - 0.5f) <= 0x1p-14f;  // NaN y: not near, rint gives NaN
+        r[c] = rintf(y);
+        any = any || exact[c];
+    }
+    if (__any(any)) {                                   // wave-uniform
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (exact[c]) r[c] = rintf(x[c] / scale);  // ties to even
+    }
     uint32_t packed = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        float r = 0.0f;
+        float v = 0.0f;
         if (amax != 0.0f) {
-            r = rintf(x[c] / scale);  // ties to even
-            if (isnan(r)) r = 0.0f;
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            v = isnan(r[c]) ? 0.0f : r[c];
+            v = fminf(fmaxf(v, -127.0f), 127.0f);
         }
-        packed |= ((uint32_t)(int32_t)r & 0xffu) << (8 * c);
+        packed |= ((uint32_t)(int32_t)v & 0xffu) << (8 * c);
     }
     *scale_out = scale;
     return packed;

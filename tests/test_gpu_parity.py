@@ -428,3 +428,31 @@ def test_loss_scale_stops_doubling_at_2_pow_127(zf):
         st = state.read()
         assert (st.loss_scale, st.good_steps, st.step) == (ref.loss_scale, ref.good_steps, ref.step)
     assert st.loss_scale == 2.0 ** 127
+
+
+@pytest.mark.parametrize("code", [1, 2])
+def test_quant_exact_ties_and_neighbours(zf, code):
+    """Blocks whose quotients x/scale land exactly on half-integers (scale a
+    power of two: amax = 127 * 2^e), the same blocks moved one 16-bit ulp up
+    or down, and blocks with subnormal and tiny scales: the codes match the
+    oracle's rint(x / scale) bit for bit."""
+    rng = np.random.default_rng(29)
+    blocks = []
+    for e in (-12, -3, 0, 2):
+        amax = orc.from_f32(np.array([127.0 * 2.0 ** e], np.float32), code)
+        k = rng.integers(-126, 126, 255)
+        ties = orc.from_f32(((k + 0.5) * 2.0 ** e).astype(np.float32), code)
+        assert np.array_equal(orc.to_f32(ties, code), ((k + 0.5) * 2.0 ** e).astype(np.float32))
+        blocks += [np.concatenate([amax, ties]), np.concatenate([amax, ties + 1]),
+                   np.concatenate([amax, ties - 1])]
+    for amax in (1e-38, 3e-39, 1e-40, 1e-44):      # scale subnormal / 1/scale overflowing
+        v = np.concatenate([[amax], rng.uniform(-amax, amax, 255)]).astype(np.float32)
+        blocks.append(orc.from_f32(v, code))
+    x = np.concatenate(blocks).astype(np.uint16)
+    n = x.size
+    q = torch.zeros(n, dtype=torch.int8, device="cuda")
+    s = torch.zeros(-(-n // 256), device="cuda")
+    zf.zero_quant_allgather_slot(to_dev(x, code), q, s)
+    rq, rs = orc.quant_int8(x, code, 256)
+    assert_bitwise(to_host(q).view(np.uint8), rq.view(np.uint8), "codes")
+    assert_bitwise(to_host(s), rs, "scales")
