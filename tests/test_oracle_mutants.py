@@ -66,6 +66,8 @@ MUTANTS = [
      "s->good_steps = 0;\n        s->step += 1;\n        return;", STEP),
     ("int8_scale_128", "const float scale = amax / 127.0f;",
      "const float scale = amax / 128.0f;", STEP),
+    ("int8_half_away_from_zero", "float r = std::nearbyint(load_elem(x, dtype, j) / scale);",
+     "float r = std::round(load_elem(x, dtype, j) / scale);", STEP),
     ("int8_truncates", "float r = std::nearbyint(load_elem(x, dtype, j) / scale);",
      "float r = std::trunc(load_elem(x, dtype, j) / scale);", STEP),
     ("round_half_up", "if (rem > half || (rem == half && (n & 1ull))) n += 1;",

@@ -373,6 +373,19 @@ def test_int8_closed_forms(orc):
     assert s[0] == 0.0 and not q.any()
 
 
+def test_int8_ties_round_to_even(orc):
+    """amax = 127 * 2^-3 makes scale = 2^-3 exactly, so x = (k + 1/2) * 2^-3
+    gives the quotient k + 1/2 exactly: the code is the even neighbour
+    (Python's round() rounds half to even)."""
+    k = np.arange(-126, 126)
+    x = np.concatenate([[127 * 0.125], (k + 0.5) * 0.125]).astype(np.float32)[:256]
+    for code in (orc.F16, orc.BF16):
+        q, s = orc.quant_int8(orc.from_f32(x, code), code, 256)
+        assert s[0] == 0.125
+        assert q[0] == 127
+        assert [int(c) for c in q[1:]] == [round(v) for v in (k[:255] + 0.5)]
+
+
 def test_int8_absmax_and_error_bound(orc):
     rng = np.random.default_rng(13)
     n = 256 * 7 + 93                                  # short last block
