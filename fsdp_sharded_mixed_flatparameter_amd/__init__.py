@@ -138,6 +138,20 @@ def _contig(t, name):
     return t
 
 
+_F16_BF16 = ("float16", "bfloat16")
+_FLOATS = ("float32", "float16", "bfloat16")
+
+
+def _dev(t, name, dtypes=None):
+    """A device argument: a contiguous CUDA tensor of one of `dtypes` (names)."""
+    _contig(t, name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device (CUDA) tensor" % name)
+    if dtypes is not None and str(t.dtype).replace("torch.", "") not in dtypes:
+        raise ValueError("%s must be %s, not %s" % (name, " or ".join(dtypes), t.dtype))
+    return t
+
+
 # ------------------------------------------------------------------ layout
 def zero_flat_layout(numels, n_ranks, align=1, param_bytes=2, grad_bytes=2, optim_bytes=12,
                      rank=0):
@@ -202,7 +216,12 @@ class StepState:
 def _state_ptr(state):
     if state is None:
         return None
-    return state.ptr() if isinstance(state, StepState) else C.c_void_p(state.data_ptr())
+    if isinstance(state, StepState):
+        return state.ptr()
+    _dev(state, "state", ("uint8",))
+    if state.numel() < STATE_BYTES:
+        raise ValueError("state must hold %d bytes" % STATE_BYTES)
+    return C.c_void_p(state.data_ptr())
 
 
 # ------------------------------------------------------------------ the step
@@ -211,13 +230,13 @@ def _rank_buffers(grad_bufs, elem_offset, shard_numel, out):
         raise ValueError("grad_bufs is empty")
     dt = _dtype_code(grad_bufs[0])
     for k, b in enumerate(grad_bufs):
-        _contig(b, "grad_bufs[%d]" % k)
+        _dev(b, "grad_bufs[%d]" % k, _FLOATS)
         if _dtype_code(b) != dt:
             raise ValueError("grad_bufs dtypes differ")
         if elem_offset + shard_numel > b.numel():
             raise ValueError("grad_bufs[%d] is shorter than elem_offset + shard_numel" % k)
-    _contig(out, "output shard")
-    if _dtype_code(out) != ZERO_F32 or out.numel() < shard_numel:
+    _dev(out, "output shard", ("float32",))
+    if out.numel() < shard_numel:
         raise ValueError("the output shard must be float32 with >= shard_numel elements")
     return dt, (C.c_void_p * len(grad_bufs))(*[b.data_ptr() for b in grad_bufs])
 
@@ -242,8 +261,10 @@ def zero_grad_accumulate_shard(grad_bufs, elem_offset, shard_numel, op, acc, sta
 
 
 def zero_unscale_norm(grad_shard, state, n=None, stream=None):
-    _contig(grad_shard, "grad_shard")
+    _dev(grad_shard, "grad_shard", _FLOATS)
     n = grad_shard.numel() if n is None else n
+    if not 0 <= n <= grad_shard.numel():
+        raise ValueError("n exceeds grad_shard")
     _check(_lib.zero_unscale_norm(_ptr(grad_shard), _dtype_code(grad_shard), n,
                                   _state_ptr(state), _stream(stream)))
 
@@ -254,9 +275,13 @@ def zero_adamw_shard_step(grad_shard, master, exp_avg, exp_avg_sq, allgather_buf
     """Skip-on-overflow, clip, AdamW on master/m/v, write-back into
     allgather_buf[slot_offset:], optional INT8 payload, scaler update."""
     n = master.numel()
-    for name, t in (("grad_shard", grad_shard), ("master", master), ("exp_avg", exp_avg),
-                    ("exp_avg_sq", exp_avg_sq), ("allgather_buf", allgather_buf)):
-        _contig(t, name)
+    _dev(grad_shard, "grad_shard", _FLOATS)
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _dev(t, name, ("float32",))
+    _dev(allgather_buf, "allgather_buf", _F16_BF16)
+    if q_buf is not None:
+        _dev(q_buf, "q_buf", ("int8",))
+        _dev(q_scales, "q_scales", ("float32",))
     if grad_shard.numel() < n or exp_avg.numel() != n or exp_avg_sq.numel() != n:
         raise ValueError("shard tensors disagree in size")
     if slot_offset + n > allgather_buf.numel():
@@ -275,8 +300,12 @@ def zero_adamw_shard_step(grad_shard, master, exp_avg, exp_avg_sq, allgather_buf
 
 def zero_quant_allgather_slot(slot, q_buf, q_scales, q_slot_offset=0, q_scale_offset=0,
                               block=256, n=None, stream=None):
-    _contig(slot, "slot")
+    _dev(slot, "slot", _F16_BF16)
+    _dev(q_buf, "q_buf", ("int8",))
+    _dev(q_scales, "q_scales", ("float32",))
     n = slot.numel() if n is None else n
+    if not 0 <= n <= slot.numel():
+        raise ValueError("n exceeds the slot")
     if q_slot_offset + n > q_buf.numel() or q_scale_offset + (n + block - 1) // block > q_scales.numel():
         raise ValueError("INT8 slot exceeds its buffers")
     _check(_lib.zero_quant_allgather_slot(_ptr(slot), _dtype_code(slot), n, block, _ptr(q_buf),
@@ -296,15 +325,13 @@ def zero_grad_reduce_shard_int8(q_slices, scale_slices, shard_numel, op, red_out
         raise ValueError("need one codes and one scales tensor per rank")
     nb = (shard_numel + block - 1) // block
     for k, (q, sc) in enumerate(zip(q_slices, scale_slices)):
-        _contig(q, "q_slices[%d]" % k)
-        _contig(sc, "scale_slices[%d]" % k)
-        if q.dtype != torch.int8 or sc.dtype != torch.float32:
-            raise ValueError("codes must be int8 and scales float32")
+        _dev(q, "q_slices[%d]" % k, ("int8",))
+        _dev(sc, "scale_slices[%d]" % k, ("float32",))
         if q.numel() < shard_numel or sc.numel() < nb:
             raise ValueError("rank %d's payload is shorter than the shard" % k)
-    _contig(red_out, "red_out")
-    if _dtype_code(red_out) != ZERO_F32 or red_out.numel() < shard_numel:
-        raise ValueError("red_out must be float32 with >= shard_numel elements")
+    _dev(red_out, "red_out", ("float32",))
+    if red_out.numel() < shard_numel:
+        raise ValueError("red_out must hold >= shard_numel elements")
     n = len(q_slices)
     qa = (C.c_void_p * n)(*[q.data_ptr() for q in q_slices])
     sa = (C.c_void_p * n)(*[sc.data_ptr() for sc in scale_slices])
@@ -329,6 +356,9 @@ def zero_offload_adamw_host(grad, master, exp_avg, exp_avg_sq, lp_out, hp, host_
     for name, t in (("grad", grad), ("master", master), ("exp_avg", exp_avg),
                     ("exp_avg_sq", exp_avg_sq), ("lp_out", lp_out)):
         _host(t, name)
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        if t.dtype.itemsize != 4 or not t.is_floating_point():
+            raise ValueError("%s must be float32" % name)
     if grad.numel() < n or exp_avg.numel() != n or exp_avg_sq.numel() != n or lp_out.numel() < n:
         raise ValueError("host tensors disagree in size")
     h = hp if isinstance(hp, zero_adamw_hparams_t) else zero_adamw_hparams_t(**hp)
@@ -346,8 +376,8 @@ def zero_offload_step(grad_shard, master, exp_avg, exp_avg_sq, grad_stage, lp_st
     parameters back into allgather_buf[slot_offset:], then the device
     loss-scaler update.  Blocks until done."""
     n = master.numel()
-    _contig(grad_shard, "grad_shard")
-    _contig(allgather_buf, "allgather_buf")
+    _dev(grad_shard, "grad_shard", _FLOATS)
+    _dev(allgather_buf, "allgather_buf", _F16_BF16)
     for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq),
                     ("grad_stage", grad_stage), ("lp_stage", lp_stage)):
         _host(t, name)
@@ -372,11 +402,9 @@ def zero_offload_step(grad_shard, master, exp_avg, exp_avg_sq, grad_stage, lp_st
 def zero_dequant_allgather(q_buf, q_scales, n_slots, slot_numel, out, block=256, stream=None):
     """out[s*S + i] = round(f32(q) * scale) over the n_slots gathered INT8 slots
     (the full flat parameter, fp16/bf16 or fp32)."""
-    for name, t in (("q_buf", q_buf), ("q_scales", q_scales), ("out", out)):
-        _contig(t, name)
-    import torch
-    if q_buf.dtype != torch.int8 or q_scales.dtype != torch.float32:
-        raise ValueError("q_buf must be int8 and q_scales float32")
+    _dev(q_buf, "q_buf", ("int8",))
+    _dev(q_scales, "q_scales", ("float32",))
+    _dev(out, "out", _FLOATS)
     nb = (slot_numel + block - 1) // block
     if q_buf.numel() < n_slots * slot_numel or q_scales.numel() < n_slots * nb or \
             out.numel() < n_slots * slot_numel:

@@ -373,8 +373,14 @@ def test_bad_arguments_raise(zf):
     state = zf.StepState(1.0, False)
     with pytest.raises(ValueError):
         zf.zero_adamw_shard_step(p, p, p, p, ag, 1, HP, state)      # slot past the end
-    with pytest.raises(zf.ZeroError):
+    with pytest.raises(ValueError):      # the binding refuses an fp32 All-Gather buffer
         zf.zero_adamw_shard_step(p, p, p, p, p.view(torch.int32).float(), 0, HP, state)
+    # and so does the library itself, through the C ABI
+    import ctypes as C
+    h = zf.zero_adamw_hparams_t(**HP)
+    P = lambda t: C.c_void_p(t.data_ptr())  # noqa: E731
+    assert zf.lib().zero_adamw_shard_step(P(p), 0, P(p), P(p), P(p), n, P(p), 0, 0, None, None,
+                                          0, 0, 256, C.byref(h), 1, state.ptr(), None) == -1
     with pytest.raises(ValueError):
         zf.zero_grad_reduce_shard([ag], 1, n, zf.ZERO_AVG, p, state)
 
