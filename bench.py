@@ -281,6 +281,47 @@ def run_workload(zf, torch, w, steps, warmup):
             "step_frac_of_peak": bpp * S / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
 
+def run_graph(zf, torch, w, steps, warmup):
+    """A whole step (reduce with statistics, AdamW, write-back, finalize)
+    captured once as a HIP graph and replayed: for launch-bound shards."""
+    from synth import synth
+    from synth.workloads import key_grad, key_master
+    S, dev = w.shard, torch.device("cuda:0")
+    master = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.fill_normal(master, key_master(w), w.start, w.master_sigma)
+    opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic)
+    grads = []
+    for k in range(w.n_ranks):
+        b = torch.empty(S, dtype=torch.float16, device=dev)
+        synth.fill_normal(b, key_grad(w, 0, k), w.start, w.grad_sigma)
+        grads.append(b)
+    ag = torch.zeros(w.padded, dtype=torch.float16, device=dev)
+    opt.step_from_rank_buffers(grads, 0, ag, w.start, op=w.op)      # warm-up, outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            opt.step_from_rank_buffers(grads, 0, ag, w.start, op=w.op)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = opt.state.read()
+    assert st.last_skipped == 0 and st.step == 1 + warmup + steps
+    del graph, opt, grads, ag, master
+    torch.cuda.empty_cache()
+    ms = wall / steps * 1e3
+    return {"ms_per_step": ms, "params_per_s": S / (ms * 1e-3),
+            "what": "the same step captured once as a HIP graph and replayed"}
+
+
 def run_gather(zf, torch, g, steps, warmup):
     """The INT8 All-Gather consumer on a gathered payload resident in HBM:
     every launch dequantises all n_ranks slots into the full flat buffer."""
@@ -471,6 +512,8 @@ def main():
             r = run_workload(zf, torch, WORKLOADS[name], max(3, args.steps // 2), 2)
             r["what"] = what
             out["variants"][name] = r
+        out["variants"]["tiny_mlp_n4_graph"] = run_graph(zf, torch, WORKLOADS["tiny_mlp_n4"],
+                                                         max(20, args.steps), 5)
         out["offload"] = run_offload(zf, torch, w, 3, 1)
         from synth.workloads import GATHERS
         out["allgather_consumer"] = {}
