@@ -18,7 +18,7 @@ ZERO_F32, ZERO_F16, ZERO_BF16 = 0, 1, 2
 ZERO_SUM, ZERO_AVG = 0, 1
 ZERO_STEP_FINALIZE = 1
 ZERO_MAX_RANKS = 256
-ZERO_MAX_PARTIALS = 2048
+ZERO_MAX_PARTIALS = 65536
 
 EXPORTS = ("zero_last_error", "zero_flat_layout", "zero_step_state_init",
            "zero_grad_reduce_shard", "zero_unscale_norm", "zero_adamw_shard_step",

@@ -29,6 +29,7 @@
 // dispatcher balances blocks as they retire.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "zf_launch.h"
 
@@ -205,7 +206,7 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // statistics of u = red * (1/loss_scale): per-block fp64 partial of u^2 into
 // st->partials[block] and an overflow flag.  A fold kernel adds the partials
 // into st->sumsq in a fixed order, so the sum is reproducible.  The partials
-// bound the grid (at most ZERO_MAX_PARTIALS blocks), so waves loop over tiles.
+// bound the grid (at most ZERO_MAX_PARTIALS blocks).
 //
 // Mapping (quad, as the AdamW kernel): in chunk j of a tile, lane l owns
 // elements 256j + 4l .. 4l+3, so every wave instruction covers one contiguous
@@ -213,18 +214,16 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // that leaves half of each cache line to another instruction costs about a
 // third of the bandwidth here.
 //
-// Work split: the grid is persistent (one partial per block), and wave w
-// walks runs of R consecutive tiles: run w, then run w + nwaves, ...  So the
-// waves resident at one time work in one window of the arrays.  Measured on
-// the 10B/8 shard: R = 2 beats one contiguous run per wave by 5% (8 fp16
-// buffers) to 7% (64 buffers); the INT8 source, with its scale loads, does best
-// at R = 16 (+6%).
+// Work split: wave w walks runs of R consecutive tiles, run w, then run
+// w + nwaves, ...  The launcher sizes the grid so that each wave has one run
+// (about 16 steps), unless the shard needs more blocks than the state holds
+// partials.
 //
 // Pipelining: a wave walks (tile, group of KC buffers) pairs in order and
 // issues the reads of the next pair before adding the current one and before
 // storing a finished tile; a scheduling barrier keeps the compiler from sinking
 // them.  KC divides N (chosen by the launcher), so no group is partial and the
-// loop body has no per-buffer branches.
+// loop body has no per-buffer branches; G1 marks N == KC (one group).
 //
 // Sources: a RawQuad<DT> holds one lane's four inputs of one rank buffer as
 // loaded (load) and adds their values to the accumulators (add_to); one()
@@ -238,14 +237,29 @@ __device__ __forceinline__ int64_t block_of(const ReduceLaunch& a, int64_t i) {
     return a.block_shift >= 0 ? (i >> a.block_shift) : i / a.block;
 }
 
+// p + e0 + off, for a wave-uniform tile start e0 and a small per-lane element
+// offset: the compiler keeps p + e0 in scalar registers and the lane's 32-bit
+// byte offset in one vector register (the scalar-base addressing form), so no
+// lane holds a 64-bit address per buffer.
+template <typename T>
+__device__ __forceinline__ T* lane_ptr(T* p, int64_t e0, uint32_t off) {
+    typedef typename std::conditional<std::is_const<T>::value, const char, char>::type Byte;
+    return reinterpret_cast<T*>(reinterpret_cast<Byte*>(p + e0) + off * (uint32_t)sizeof(T));
+}
+
+// Four consecutive elements of one rank's buffer at tile start e0 + lane
+// offset off (elements).
 template <int DT>
 struct RawQuad;
 template <>
 struct RawQuad<ZERO_F32> {
     v4f x;
-    __device__ __forceinline__ void load_ptr(const float* p, int64_t i) { x = ldnt_f4(p + i); }
-    __device__ __forceinline__ void load(const ReduceLaunch& a, int k, int64_t i, int64_t) {
-        load_ptr(static_cast<const float*>(a.bufs[k]), i);
+    __device__ __forceinline__ void load_ptr(const float* p, int64_t e0, uint32_t off) {
+        x = ldnt_f4(lane_ptr(p, e0, off));
+    }
+    __device__ __forceinline__ void load(const ReduceLaunch& a, int k, int64_t e0, uint32_t off,
+                                         int64_t) {
+        load_ptr(static_cast<const float*>(a.bufs[k]), e0, off);
     }
     __device__ __forceinline__ void add_to(float acc[4]) const {
         acc[0] = acc[0] + x.x; acc[1] = acc[1] + x.y; acc[2] = acc[2] + x.z; acc[3] = acc[3] + x.w;
@@ -258,10 +272,11 @@ template <>
 struct RawQuad<kQ8> {
     uint32_t w;  // four codes
     float s;     // their block's scale (4 | block: a quad never straddles blocks)
-    // bi: the block of element i, the same for every rank (computed once per chunk)
-    __device__ __forceinline__ void load(const ReduceLaunch& a, int k, int64_t i, int64_t bi) {
-        w = __builtin_nontemporal_load(
-            reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(a.bufs[2 * k]) + i));
+    // bi: the block of the quad, the same for every rank (computed once per chunk)
+    __device__ __forceinline__ void load(const ReduceLaunch& a, int k, int64_t e0, uint32_t off,
+                                         int64_t bi) {
+        w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
+            lane_ptr(static_cast<const int8_t*>(a.bufs[2 * k]), e0, off)));
         s = static_cast<const float*>(a.bufs[2 * k + 1])[bi];
     }
     __device__ __forceinline__ void add_to(float acc[4]) const {
@@ -277,8 +292,9 @@ struct RawQuad<kQ8> {
 template <int DT>
 struct RawQuad {
     v2u w;
-    __device__ __forceinline__ void load(const ReduceLaunch& a, int k, int64_t i, int64_t) {
-        w = ldnt_u2(static_cast<const uint16_t*>(a.bufs[k]) + i);
+    __device__ __forceinline__ void load(const ReduceLaunch& a, int k, int64_t e0, uint32_t off,
+                                         int64_t) {
+        w = ldnt_u2(lane_ptr(static_cast<const uint16_t*>(a.bufs[k]), e0, off));
     }
     __device__ __forceinline__ void add_to(float acc[4]) const {
         acc[0] = acc[0] + cvt16<DT>(w.x & 0xffffu);
@@ -291,7 +307,7 @@ struct RawQuad {
     }
 };
 
-template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC>
+template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float inv_n,
                                                           int pow2_n, int run_tiles) {
     static_assert(WRITE || !ACC, "accumulation writes its output");
@@ -301,7 +317,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const int64_t n = a.n;
     const int N = a.n_ranks;
-    const int ngroups = N / KC;
+    const int ngroups = G1 ? 1 : N / KC;   // G1: the N buffers form one group
     const bool avg = a.op == ZERO_AVG;
     float inv_scale = 1.0f;
     if constexpr (STATS) inv_scale = (float)(1.0 / (double)a.st->loss_scale);
@@ -315,11 +331,12 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
     double ss0 = 0.0, ss1 = 0.0;
 
     // prev: the shard's accumulated values for these elements (ACC only)
-    auto finish = [&](const float (&acc)[TU][4], const float (&prev)[TU][4], int64_t base,
-                      bool full) {
+    // the quads of the tile at e0 that this lane owns start at e0 + lo + 256 j
+    auto finish = [&](const float (&acc)[TU][4], const float (&prev)[TU][4], int64_t e0,
+                      uint32_t lo, bool full) {
 #pragma unroll
         for (int j = 0; j < TU; ++j) {
-            const int64_t i0 = base + 256 * j;
+            const int64_t i0 = e0 + lo + 256 * j;
             float red[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -329,7 +346,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
             }
             if constexpr (WRITE) {
                 if (full) {
-                    stnt_f4(a.red_out + i0, red[0], red[1], red[2], red[3]);
+                    stnt_f4(lane_ptr(a.red_out, e0, lo + 256 * j), red[0], red[1], red[2], red[3]);
                 } else {
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
@@ -351,76 +368,114 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
 
     const int64_t ntiles = (n + kT - 1) / kT;
     const int64_t nfull = VEC ? n / kT : 0;
-    // ---- full tiles: wave w owns tiles [w*per, min((w+1)*per, nfull))
-    // Wave w walks runs of R consecutive tiles: run w, then run w + nwaves, ...
+    // ---- full tiles.  A step is one (tile, buffer group) pair.  Wave w walks
+    // runs of R consecutive tiles: run w, then run w + nwaves, ...; inside a
+    // tile it walks the buffer groups in rank order.
+    //
+    // Software pipeline: the next step's reads are issued before the current
+    // step's adds and stores.  Two register sets A and B swap roles every
+    // step (the loop body is a pair of steps), so no register copy has to
+    // wait for reads in flight.  The wave's step count is known up front, so
+    // the loop body holds no exit and no conditional read; the last one or
+    // two steps run after it.  The compiler then waits for exactly the reads
+    // the adds need and keeps the next step's reads (and earlier stores) in
+    // flight.
     const int64_t R = run_tiles;
-    const int64_t t_begin = wave_id * R;
-    if (t_begin < nfull) {
-        RawQuad<DT> cur[KC][TU], nxt[KC][TU];
-        RawQuad<ZERO_F32> pcur[TU], pnxt[TU];   // accumulator quads (ACC only)
+    if (wave_id * R < nfull) {
+        RawQuad<DT> xa[KC][TU], xb[KC][TU];
+        RawQuad<ZERO_F32> pa[TU], pb[TU];   // accumulator quads (ACC only)
+        const uint32_t lo = 4 * lane;
         auto load_group = [&](RawQuad<DT> (&x)[KC][TU], RawQuad<ZERO_F32> (&px)[TU], int64_t tt,
                               int gg) {
-            const int64_t base = tt * kT + 4 * lane;
+            const int64_t e0 = tt * kT;
             int64_t bi[TU];
 #pragma unroll
-            for (int j = 0; j < TU; ++j) bi[j] = DT == kQ8 ? block_of(a, base + 256 * j) : 0;
+            for (int j = 0; j < TU; ++j) bi[j] = DT == kQ8 ? block_of(a, e0 + lo + 256 * j) : 0;
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk)
 #pragma unroll
-                for (int j = 0; j < TU; ++j) x[kk][j].load(a, gg * KC + kk, base + 256 * j, bi[j]);
-            if constexpr (ACC) {
-                if (gg == 0) {
+                for (int j = 0; j < TU; ++j) x[kk][j].load(a, gg * KC + kk, e0, lo + 256 * j, bi[j]);
+            if constexpr (ACC) {   // the shard's values, with the group that finishes the tile
+                if (G1 || gg == ngroups - 1) {
 #pragma unroll
-                    for (int j = 0; j < TU; ++j) px[j].load_ptr(a.red_out, base + 256 * j);
+                    for (int j = 0; j < TU; ++j) px[j].load_ptr(a.red_out, e0, lo + 256 * j);
                 }
             }
         };
-        load_group(cur, pcur, t_begin, 0);
-        int64_t t = t_begin;
-        int64_t left = R;  // tiles of the current run still to finish, t included
-        int g = 0;
         float acc[TU][4];
 #pragma unroll
         for (int j = 0; j < TU; ++j)
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[j][c] = 0.0f;
-        for (;;) {
-            // the pair after (t, g); past the run's end it re-reads the last
-            // pair (harmless, in bounds, never used)
-            int gn = g + 1;
-            int64_t tn = t;
-            if (gn == ngroups) {
-                gn = 0;
-                tn = left == 1 ? t + 1 + (nwaves - 1) * R : t + 1;
-            }
-            const bool more = tn < nfull;
-            load_group(nxt, pnxt, more ? tn : t, more ? gn : g);
-            __builtin_amdgcn_sched_barrier(0);
+        // add the group held in x; the tile's last group also finishes it
+        auto consume = [&](const RawQuad<DT> (&x)[KC][TU], const RawQuad<ZERO_F32> (&px)[TU],
+                           int64_t tt, int gg) {
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk)                  // rank order per element
 #pragma unroll
-                for (int j = 0; j < TU; ++j) cur[kk][j].add_to(acc[j]);
-            if (gn == 0) {                                   // tile t complete
+                for (int j = 0; j < TU; ++j) x[kk][j].add_to(acc[j]);
+            if (G1 || gg == ngroups - 1) {
                 float prev[TU][4];
 #pragma unroll
                 for (int j = 0; j < TU; ++j) {
-                    prev[j][0] = pcur[j].x.x; prev[j][1] = pcur[j].x.y;
-                    prev[j][2] = pcur[j].x.z; prev[j][3] = pcur[j].x.w;
+                    prev[j][0] = px[j].x.x; prev[j][1] = px[j].x.y;
+                    prev[j][2] = px[j].x.z; prev[j][3] = px[j].x.w;
                 }
-                finish(acc, prev, t * kT + 4 * lane, true);
+                finish(acc, prev, tt * kT, lo, true);
 #pragma unroll
                 for (int j = 0; j < TU; ++j)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) acc[j][c] = 0.0f;
             }
-            if (!more) break;
-            __builtin_memcpy(cur, nxt, sizeof(cur));         // register renaming
-            if constexpr (ACC) {
-                if (gn == 0) __builtin_memcpy(pcur, pnxt, sizeof(pcur));
+        };
+        // this wave's full tiles: runs start at w*R + j*nwaves*R; every run
+        // but the last holds R tiles
+        const int64_t span = nwaves * R;
+        const int64_t q = nfull - wave_id * R;           // > 0 here
+        const int64_t runs = (q + span - 1) / span;
+        const int64_t last = q - (runs - 1) * span;
+        const int64_t nsteps = ((runs - 1) * R + (last < R ? last : R)) * ngroups;
+        int64_t t = wave_id * R, left = R;
+        int g = 0;
+        auto advance = [&]() {   // (t, g) := the step after (t, g)
+            ++g;
+            if (G1 || g == ngroups) {
+                g = 0;
+                if (left == 1) {
+                    t += 1 + (nwaves - 1) * R;
+                    left = R;
+                } else {
+                    t += 1;
+                    --left;
+                }
             }
-            if (gn == 0) left = left == 1 ? R : left - 1;
-            t = tn;
-            g = gn;
+        };
+        load_group(xa, pa, t, g);
+        int64_t k = 0;                                    // A holds step k
+        for (; k + 2 < nsteps; k += 2) {                  // steps k+1 and k+2 exist
+            const int64_t t0 = t;
+            const int g0 = g;
+            advance();
+            load_group(xb, pb, t, g);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(xa, pa, t0, g0);
+            const int64_t t1 = t;
+            const int g1 = g;
+            advance();
+            load_group(xa, pa, t, g);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(xb, pb, t1, g1);
+        }
+        if (k + 1 < nsteps) {                             // two steps left
+            const int64_t t0 = t;
+            const int g0 = g;
+            advance();
+            load_group(xb, pb, t, g);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(xa, pa, t0, g0);
+            consume(xb, pb, t, g);
+        } else {
+            consume(xa, pa, t, g);
         }
     }
     // ---- the ragged tail (or every tile, without the vector path): element-wise
@@ -448,7 +503,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
                 const int64_t i = base + 256 * j + c;
                 prev[j][c] = (ACC && i < n) ? a.red_out[i] : 0.0f;
             }
-        finish(acc, prev, base, false);
+        finish(acc, prev, t * kT, 4 * lane, false);
     }
     if constexpr (STATS) {
         const double mine = ss0 + ss1;
@@ -769,35 +824,36 @@ int grid_for_tiles(int64_t ntiles, int cap) {
     return (int)g;
 }
 
-// Blocks of `kernel` resident at once on the current device (CUs x blocks
-// per CU at the kernel's register occupancy), cached per device.
-template <typename K>
-int resident_blocks(K kernel) {
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cache[dev] > 0) return cache[dev];
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
-        return 0;
-    cache[dev] = cus * per_cu;
-    return cache[dev];
+// The reduce grid: every wave takes one run of R consecutive tiles and the
+// hardware dispatcher issues the blocks in order, so the tiles in flight at
+// any moment form one narrow window of each buffer.  (A persistent grid whose
+// waves walk the shard measured 5-10% slower: its waves drift apart and the
+// reads in flight spread over the buffers.)  R aims at kRunSteps steps per
+// wave (a step is one tile of one buffer group), shrinks so that small shards
+// still launch kFillBlocks blocks, and grows when the blocks would outnumber
+// the state's per-block partial sums (ZERO_MAX_PARTIALS).
+constexpr int64_t kRunSteps = 16;
+constexpr int64_t kFillBlocks = 2048;
+template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
+void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
+    const int64_t ntiles = (a.n + 256 * TU - 1) / (256 * TU);
+    const int64_t ngroups = G1 ? 1 : a.n_ranks / KC;
+    int64_t run = kRunSteps / ngroups;
+    const int64_t fill = ntiles / (kWaves * kFillBlocks);
+    if (run > fill) run = fill;
+    if (run < 1) run = 1;
+    const int64_t need = (ntiles + kWaves * kMaxGridReduce - 1) / (kWaves * kMaxGridReduce);
+    if (run < need) run = need;
+    int64_t grid = (ntiles + kWaves * run - 1) / (kWaves * run);
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((reduce_kernel<DT, VEC, WRITE, STATS, TU, KC, ACC, G1>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, (hipStream_t)stream, a, inv_n, pow2, (int)run);
 }
 
-// The reduce grid is persistent (one partial sum per block, at most
-// ZERO_MAX_PARTIALS blocks): a whole number of resident rounds, so that no
-// partly filled last round leaves the machine idle while it drains.
 template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC>
 void launch_reduce_shape(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
-    auto kernel = reduce_kernel<DT, VEC, WRITE, STATS, TU, KC, ACC>;
-    const int64_t ntiles = (a.n + 256 * TU - 1) / (256 * TU);
-    int grid = grid_for_tiles(ntiles, kMaxGridReduce);
-    const int round = resident_blocks(kernel);
-    if (round > 0 && grid > round) grid = (grid / round) * round;
-    const int run = DT == kQ8 ? 16 : 2;  // tiles per run (see reduce_kernel)
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, a, inv_n,
-                       pow2, run);
+    if (a.n_ranks == KC) launch_reduce_grid<DT, VEC, WRITE, STATS, TU, KC, ACC, true>(a, stream, inv_n, pow2);
+    else launch_reduce_grid<DT, VEC, WRITE, STATS, TU, KC, ACC, false>(a, stream, inv_n, pow2);
 }
 
 template <int DT, bool VEC, bool WRITE, bool STATS, bool ACC>

@@ -19,6 +19,7 @@
 // as soon as its copy has landed, and its 16-bit parameters move host-to-device
 // into the All-Gather slot while later chunks are still being computed.
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -26,6 +27,7 @@
 #include <atomic>
 #include <condition_variable>
 #include <functional>
+#include <memory>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -244,9 +246,12 @@ int offload_step(const OffloadLaunch& a, const zero_adamw_hparams_t& hp, void* s
     hipStream_t stream = (hipStream_t)stream_v;
     const int64_t es = a.gdtype == ZERO_F32 ? 4 : 2;
     const int64_t nch = a.n == 0 ? 0 : (a.n + a.chunk - 1) / a.chunk;
-    zero_step_state_t st;
+    // the scalars of the state (everything before the per-block partials)
+    std::unique_ptr<zero_step_state_t> host_st(new zero_step_state_t);
+    zero_step_state_t& st = *host_st;
     hipEvent_t ev_state = nullptr;
-    hipError_t e = hipMemcpyAsync(&st, a.st, sizeof st, hipMemcpyDeviceToHost, stream);
+    hipError_t e = hipMemcpyAsync(&st, a.st, offsetof(zero_step_state_t, partials),
+                                  hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_state, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventRecord(ev_state, stream);
     std::vector<hipEvent_t> ev(nch, nullptr);

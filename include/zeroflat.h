@@ -77,7 +77,7 @@ typedef enum { ZERO_F32 = 0, ZERO_F16 = 1, ZERO_BF16 = 2 } zero_dtype_t;
 typedef enum { ZERO_SUM = 0, ZERO_AVG = 1 } zero_reduce_op_t;
 
 #define ZERO_MAX_RANKS 256      /* gradient buffers one reduce call can read */
-#define ZERO_MAX_PARTIALS 2048  /* per-block partial sums kept in the state */
+#define ZERO_MAX_PARTIALS 65536 /* per-block partial sums kept in the state */
 
 /* Message for the last failure on this thread ("" if none). */
 const char* zero_last_error(void);
@@ -133,8 +133,9 @@ int zero_flat_layout(const int64_t* numels, int32_t n_params, int32_t n_ranks, i
 
 /* ------------------------------------------------------------------------
  * Step state.  Device-resident, caller-allocated (sizeof(zero_step_state_t)
- * bytes, 8-byte aligned), initialised from a host copy filled by
- * zero_step_state_init.  The library reads and updates it on the stream, so
+ * bytes, about 512 KiB, 8-byte aligned; most of it is the table of per-block
+ * partial sums of the statistics kernels), initialised from a host copy
+ * filled by zero_step_state_init.  The library reads and updates it on the stream, so
  * the skip and loss-scale decisions never leave the device.
  * ---------------------------------------------------------------------- */
 typedef struct {
