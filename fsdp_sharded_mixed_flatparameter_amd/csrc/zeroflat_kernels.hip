@@ -518,12 +518,35 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
 }
 
 // st->sumsq += partials[0..n_partials), fixed order (one block)
-__global__ void __launch_bounds__(kThreads) fold_kernel(zero_step_state_t* st) {
+// One block of kFoldThreads: thread t adds partials t, t + kFoldThreads, ...
+// in that order, with kFoldU loads in flight (an out-of-range slot adds +0,
+// which leaves a sum of non-negative terms unchanged); then the waves'
+// butterflies and the waves in index order.
+constexpr int kFoldThreads = 1024;
+constexpr int kFoldU = 8;
+__global__ void __launch_bounds__(kFoldThreads) fold_kernel(zero_step_state_t* st) {
     const int n = st->n_partials;
     double s = 0.0;
-    for (int i = threadIdx.x; i < n; i += kThreads) s += st->partials[i];
-    s = block_sum(s);
-    if (threadIdx.x == 0) st->sumsq = st->sumsq + s;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kFoldThreads * kFoldU) {
+        double v[kFoldU];
+#pragma unroll
+        for (int u = 0; u < kFoldU; ++u) {
+            const int i = i0 + u * kFoldThreads;
+            v[u] = i < n ? st->partials[i] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kFoldU; ++u) s += v[u];
+    }
+    __shared__ double sh[kFoldThreads / 64];
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+#pragma unroll
+        for (int w = 0; w < kFoldThreads / 64; ++w) t += sh[w];
+        st->sumsq = st->sumsq + t;
+    }
 }
 
 // ---------------------------------------------------------------- INT8 of one slice
@@ -869,7 +892,7 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (STATS) {
-        hipLaunchKernelGGL(fold_kernel, dim3(1), dim3(kThreads), 0, (hipStream_t)stream, a.st);
+        hipLaunchKernelGGL(fold_kernel, dim3(1), dim3(kFoldThreads), 0, (hipStream_t)stream, a.st);
         e = hipGetLastError();
     }
     return (int)e;
