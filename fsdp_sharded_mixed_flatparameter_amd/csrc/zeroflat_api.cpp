@@ -322,7 +322,8 @@ int zero_quant_allgather_slot(const void* slot, int32_t dtype, int64_t n, int32_
     a.n = n;
     a.q = q_buf + q_slot_offset;
     a.qs = q_scales + q_scale_offset;
-    a.vec = (aligned(slot, 8) && aligned(a.q, 4)) ? 1 : 0;
+    // 2: eight elements per lane (16-byte slot, 8-byte codes); 1: quad tiles
+    a.vec = (aligned(slot, 16) && aligned(a.q, 8)) ? 2 : (aligned(slot, 8) && aligned(a.q, 4)) ? 1 : 0;
     const int e = zf::launch_quant(a, stream);
     if (e) return hip_fail(e, fn);
     return ok();

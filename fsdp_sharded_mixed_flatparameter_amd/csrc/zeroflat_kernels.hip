@@ -8,7 +8,8 @@
 //   fold_kernel      the statistics' per-block partial sums, in a fixed order
 //   adamw_kernel     skip/clip prologue, fused AdamW, 16-bit write-back, INT8
 //   finalize_kernel  loss scaler and counters
-//   quant_kernel     INT8 of an existing 16-bit slot
+//   quant_kernel     INT8 of an existing 16-bit slot (quad tiles)
+//   quant8_kernel    the same on 16-byte aligned slots, eight elements per lane
 //   dequant_kernel   the INT8 All-Gather consumer
 //
 // Every kernel here streams HBM once: none is a contraction, so there is no
@@ -59,6 +60,7 @@ constexpr int kMaxGridReduce = ZERO_MAX_PARTIALS;
 // accesses: every array of the step is touched exactly once per launch.
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f ldnt_f4(const float* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
@@ -764,6 +766,116 @@ __global__ void __launch_bounds__(kThreads) quant_kernel(QuantLaunch a) {
     }
 }
 
+// Standalone INT8 of a 16-bit slot with a lane mapping of its own (the AdamW
+// epilogue keeps the quad mapping of the update): a wave tile is kQChunks
+// chunks of 512 elements, and in each chunk lane l holds elements 8l .. 8l+7,
+// one 16-byte load of 16-bit values and one 8-byte store of codes; every wave
+// instruction still covers one contiguous span (1 KiB in, 512 B out).  Lanes
+// 0-31 then hold one 256-element block and lanes 32-63 the next, so a block's
+// absmax is a 5-step butterfly inside each half wave (against 6 steps per
+// four elements in the quad mapping).  The per-element arithmetic is
+// quant_quad's, so the codes and scales are the same bit for bit.
+constexpr int kQChunks = 4;
+constexpr int64_t kQTile = 512 * kQChunks;
+
+__device__ __forceinline__ float half_wave_max(float x) {
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+// x[8]: this lane's eight values (zero past the end); codes packed four per
+// word into out[0..1]; the block's scale into *scale_out
+__device__ __forceinline__ void quant_oct(const float x[8], uint32_t out[2], float* scale_out) {
+    float a = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(x[c]));
+    const float amax = half_wave_max(a);
+    const float scale = amax / 127.0f;
+    const float rs = 1.0f / scale;
+    const bool fast = isfinite(rs) && rs != 0.0f;
+    float r[8];
+    bool exact[8];
+    bool any = false;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const float y = x[c] * rs;
+        const float f = y - floorf(y);
+        exact[c] = !fast || fabsf(f - 0.5f) <= 0x1p-14f;
+        r[c] = rintf(y);
+        any = any || exact[c];
+    }
+    if (__any(any)) {                                   // wave-uniform
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            if (exact[c]) r[c] = rintf(x[c] / scale);
+    }
+    out[0] = 0;
+    out[1] = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        float v = 0.0f;
+        if (amax != 0.0f) {
+            v = isnan(r[c]) ? 0.0f : r[c];
+            v = fminf(fmaxf(v, -127.0f), 127.0f);
+        }
+        out[c >> 2] |= ((uint32_t)(int32_t)v & 0xffu) << (8 * (c & 3));
+    }
+    *scale_out = scale;
+}
+
+// x 16-byte aligned, q 8-byte aligned (checked by the host)
+template <int DT>
+__global__ void __launch_bounds__(kThreads) quant8_kernel(QuantLaunch a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_id = wave_index();
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int64_t n = a.n;
+    const int64_t ntiles = (n + kQTile - 1) / kQTile;
+    const int64_t nfull = n / kQTile;
+    const uint32_t lo = 8 * lane;
+    const uint16_t* x16 = static_cast<const uint16_t*>(a.x);
+    for (int64_t t = wave_id; t < ntiles; t += nwaves) {
+        const int64_t e0 = t * kQTile;
+        if (t < nfull) {
+            v4u w[kQChunks];
+#pragma unroll
+            for (int k = 0; k < kQChunks; ++k)
+                w[k] = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4u*>(lane_ptr(x16, e0 + 512 * k, lo)));
+#pragma unroll
+            for (int k = 0; k < kQChunks; ++k) {
+                float x[8];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    x[2 * c] = cvt16<DT>(w[k][c] & 0xffffu);
+                    x[2 * c + 1] = cvt16<DT>(w[k][c] >> 16);
+                }
+                uint32_t code[2];
+                float scale;
+                quant_oct(x, code, &scale);
+                stnt_u2(lane_ptr(a.q, e0 + 512 * k, lo), code[0], code[1]);
+                if ((lane & 31) == 0) a.qs[(e0 + 512 * k + lo) / 256] = scale;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kQChunks; ++k) {
+                const int64_t i0 = e0 + 512 * k + lo;
+                float x[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[c] = i0 + c < n ? load_one<DT>(a.x, i0 + c) : 0.0f;
+                uint32_t code[2];
+                float scale;
+                quant_oct(x, code, &scale);               // the whole wave takes part
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    if (i0 + c < n) a.q[i0 + c] = (int8_t)((code[c >> 2] >> (8 * (c & 3))) & 0xffu);
+                if ((lane & 31) == 0 && i0 < n) a.qs[i0 / 256] = scale;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- INT8 consumer
 // out[s*S + i] = round(f32(q) * scale of (slot s, block i / block)).  A wave
 // tile is kDU slices of 256 elements of one slot (tiles never straddle slots,
@@ -998,6 +1110,16 @@ int launch_dequant(const DequantLaunch& a, void* stream) {
 }
 
 int launch_quant(const QuantLaunch& a, void* stream) {
+    if (a.vec == 2) {
+        const int grid = grid_for_tiles((a.n + kQTile - 1) / kQTile, kMaxGridStream);
+        if (a.dtype == ZERO_F16)
+            hipLaunchKernelGGL((quant8_kernel<ZERO_F16>), dim3(grid), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+        else
+            hipLaunchKernelGGL((quant8_kernel<ZERO_BF16>), dim3(grid), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+        return (int)hipGetLastError();
+    }
     const int64_t ntiles = (a.n + kTile - 1) / kTile;
     const int grid = grid_for_tiles(ntiles, kMaxGridStep);
     if (a.dtype == ZERO_F16) {

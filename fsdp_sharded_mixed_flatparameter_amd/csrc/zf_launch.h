@@ -51,7 +51,8 @@ int launch_adamw(const AdamLaunch& a, void* stream);
 struct QuantLaunch {
     const void* x;
     int32_t dtype;
-    int32_t vec;
+    int32_t vec;     // 2: eight elements per lane (x 16-byte, q 8-byte aligned);
+                     // 1: quad tiles (x 8-byte, q 4-byte aligned); 0: element-wise
     int64_t n;
     int8_t* q;
     float* qs;

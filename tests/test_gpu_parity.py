@@ -210,6 +210,35 @@ def test_quant_special_blocks(zf):
     assert_bitwise(to_host(s), rs, "scales")
 
 
+@pytest.mark.parametrize("pdt", [1, 2])
+def test_quant_all_three_lane_mappings(zf, pdt):
+    """The same slot quantised by each of the library's three kernels, picked by
+    alignment: eight elements per lane (16-byte slot, 8-byte codes), quad tiles
+    (8-byte slot, 4-byte codes) and element-wise (2-byte slot).  Codes and
+    scales equal the oracle's in all three; the slot spans five full 2048-element
+    tiles and a ragged tail, with a zero block, an infinity and a constant block."""
+    n = 2048 * 5 + 700
+    nb = -(-n // 256)
+    x = orc.to_f32(synth.normal(synth.stream_key("qpaths", pdt), 0, n, 0.02, pdt), pdt)
+    x[512:768] = 0.0
+    x[3000] = np.inf
+    x[4096:4352] = 0.75
+    xs = orc.from_f32(x, pdt)
+    rq, rs = orc.quant_int8(xs, pdt, 256)
+    tdt = torch.float16 if pdt == 1 else torch.bfloat16
+    for el_off, q_off in ((8, 8), (4, 4), (1, 1)):
+        say("quant mapping: slot offset", el_off, "elements, codes offset", q_off, "bytes")
+        base = torch.zeros(el_off + n + 8, dtype=tdt, device="cuda")
+        base[el_off:el_off + n] = to_dev(xs, pdt)
+        q = torch.zeros(q_off + n + 8, dtype=torch.int8, device="cuda")
+        s = torch.zeros(nb, device="cuda")
+        zf.zero_quant_allgather_slot(base[el_off:el_off + n], q, s, q_slot_offset=q_off)
+        qh = to_host(q)
+        assert_bitwise(qh[q_off:q_off + n].view(np.uint8), rq.view(np.uint8), "codes")
+        assert not qh[:q_off].any() and not qh[q_off + n:].any()
+        assert_bitwise(to_host(s), rs, "scales")
+
+
 def test_clip_coefficient_matches_oracle(zf):
     """The fp64 clip coefficient for many global sums of squares, including
     a remote contribution, computed by the finalize stage of an empty step."""
