@@ -1000,6 +1000,7 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     if (N % 8 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
     else if (N % 4 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
     else if (N % 2 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
+    else if (N == 1) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 1, ACC>(a, stream, inv_n, pow2);
     else launch_reduce_shape<DT, VEC, WRITE, STATS, 8, 1, ACC>(a, stream, inv_n, pow2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;

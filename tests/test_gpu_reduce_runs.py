@@ -11,7 +11,7 @@ so these sizes reach, per case:
   8 INT8 payloads, 25,000,000           one group, R = 5
   4 fp16 buffers, 70,000,000            one group, R = 16 (the full run)
   2 fp32 buffers, 26,000,003            one group of two, R = 3
-  statistics pass, 40,000,001 fp16      one buffer, R = 2
+  statistics pass, 40,000,001 fp16      one buffer, R = 9
 
 and in each the last wave's run is cut short by the end of the full tiles,
 followed by the ragged tail.  Bar: the reduced (or accumulated) shard bit for
