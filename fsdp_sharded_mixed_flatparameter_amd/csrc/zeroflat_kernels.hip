@@ -996,8 +996,12 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     const int N = a.n_ranks;
     const int pow2 = (N & (N - 1)) == 0;
     const float inv_n = 1.0f / (float)N;  // exact when N is a power of two
-    // reads in flight per lane: TU chunks x KC buffers (KC divides N)
-    if (N % 8 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
+    // reads in flight per lane: TU chunks x KC buffers (KC divides N).  Many
+    // 16-bit or fp32 buffers read one chunk of 16 buffers per step (7% faster
+    // than two chunks of 8 at 64 buffers); INT8 payloads keep two chunks of 8.
+    if (DT != kQ8 && N % 16 == 0)
+        launch_reduce_shape<DT, VEC, WRITE, STATS, 1, 16, ACC>(a, stream, inv_n, pow2);
+    else if (N % 8 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
     else if (N % 4 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
     else if (N % 2 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
     else if (N == 1) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 1, ACC>(a, stream, inv_n, pow2);

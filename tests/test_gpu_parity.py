@@ -53,7 +53,7 @@ REDUCE_CASES = [
     (1, 4, 1, 513, 0), (1, 8, 1, 4096 + 13, 8), (1, 64, 1, 20_000, 0), (1, 3, 1, 1000, 0),
     (1, 3, 0, 1000, 3), (2, 8, 0, 100_000, 16), (2, 8, 1, 100_000, 16), (2, 8, 1, 9_999, 5),
     (2, 5, 1, 777, 0), (0, 4, 1, 3000, 4), (0, 2, 0, 3001, 1), (1, 1, 1, 2049, 0),
-    (1, 11, 1, 4097, 0), (2, 17, 0, 5000, 8),
+    (1, 11, 1, 4097, 0), (2, 17, 0, 5000, 8), (1, 16, 1, 5003, 0), (2, 48, 0, 3001, 8),
 ]
 
 

@@ -5,7 +5,7 @@ steps of one tile and one buffer group each, fewer when the shard is small),
 so these sizes reach, per case:
 
   8 fp16 buffers, 30,000,123 elements   one group, R = 7 (odd step count)
-  16 bf16 buffers, 20,000,001           two groups, R = 4 (8 steps)
+  32 bf16 buffers, 10,000,001           two groups of 16, R = 4 (8 steps)
   12 fp16 buffers, 10,000,007, 2 micro-steps accumulated
                                         three groups, R = 2 (6 steps)
   8 INT8 payloads, 25,000,000           one group, R = 5
@@ -62,7 +62,7 @@ def check_stats(state, red, scale):
 
 
 @pytest.mark.parametrize("dt,N,op,S,off", [
-    (1, 8, 1, 30_000_123, 8), (2, 16, 0, 20_000_001, 0), (1, 4, 1, 70_000_000, 0),
+    (1, 8, 1, 30_000_123, 8), (2, 32, 0, 10_000_001, 0), (1, 4, 1, 70_000_000, 0),
     (0, 2, 0, 26_000_003, 4)])
 def test_reduce_runs_whole_output(zf, dt, N, op, S, off):
     say("reduce runs", dt, N, op, S, off)
