@@ -464,7 +464,8 @@ def run_copy_calibration(torch, nbytes=4 << 30, reps=5):
     med = ms[len(ms) // 2]
     del src, dst
     torch.cuda.empty_cache()
-    return dict(kernel="synth copy16 (grid-stride 16-byte copy)", bytes_per_launch=2 * nbytes,
+    return dict(kernel="synth copy16 (non-temporal 16-byte copy, 16 KiB per block)",
+                bytes_per_launch=2 * nbytes,
                 ms_per_launch=med, GBps=2 * nbytes / (med * 1e-3) / 1e9)
 
 
