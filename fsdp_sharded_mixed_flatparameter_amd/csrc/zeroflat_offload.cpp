@@ -271,19 +271,45 @@ int offload_step(const OffloadLaunch& a, const zero_adamw_hparams_t& hp, void* s
     hipStream_t up = nullptr;
     if (e == hipSuccess && !skipped && a.n > 0) e = hipStreamCreateWithFlags(&up, hipStreamNonBlocking);
     if (e == hipSuccess && !skipped && a.n > 0) {
-        Pool pool(std::min<int64_t>(threads_for(a.n_threads), std::max<int64_t>(1, a.chunk / 4096)));
+        // Every thread walks all chunks in order and updates its own part of
+        // each (the same split as the host entry point) as soon as the chunk's
+        // gradient has landed; the thread that finishes a chunk last sends its
+        // parameters up.  No barrier between chunks, so a thread that is
+        // ahead goes on with the next chunk instead of waiting for the slowest.
+        const int nt = (int)std::min<int64_t>(threads_for(a.n_threads),
+                                              std::max<int64_t>(1, a.chunk / 4096));
         uint16_t* lp = static_cast<uint16_t*>(a.h_lp);
-        const std::function<void(int64_t, int64_t)> fn = [&](int64_t lo, int64_t hi) {
-            adam_range(s, a.gdtype, a.pdtype, a.h_grad, a.h_p, a.h_m, a.h_v, lp, lo, hi);
+        std::vector<std::atomic<int>> left(nch);
+        for (auto& x : left) x.store(nt);
+        std::atomic<int> err(hipSuccess);
+        auto worker = [&](int t) {
+            for (int64_t c = 0; c < nch; ++c) {
+                if (err.load(std::memory_order_relaxed) != hipSuccess) return;
+                const int64_t lo = c * a.chunk, len = std::min(a.chunk, a.n - lo);
+                hipError_t we = hipEventSynchronize(ev[c]);
+                if (we == hipSuccess) {
+                    int64_t per = (len + nt - 1) / nt;
+                    per = (per + 63) / 64 * 64;
+                    const int64_t pa = std::min(lo + len, lo + per * t);
+                    const int64_t pb = std::min(lo + len, pa + per);
+                    if (pa < pb)
+                        adam_range(s, a.gdtype, a.pdtype, a.h_grad, a.h_p, a.h_m, a.h_v, lp, pa, pb);
+                    if (left[c].fetch_sub(1) == 1)
+                        we = hipMemcpyAsync(static_cast<uint16_t*>(a.d_slot) + lo, lp + lo, len * 2,
+                                            hipMemcpyHostToDevice, up);
+                }
+                if (we != hipSuccess) {
+                    int none = hipSuccess;
+                    err.compare_exchange_strong(none, (int)we);
+                    return;
+                }
+            }
         };
-        for (int64_t c = 0; c < nch && e == hipSuccess; ++c) {
-            const int64_t lo = c * a.chunk, len = std::min(a.chunk, a.n - lo);
-            e = hipEventSynchronize(ev[c]);
-            if (e != hipSuccess) break;
-            pool.run(lo, lo + len, fn);
-            e = hipMemcpyAsync(static_cast<uint16_t*>(a.d_slot) + lo, lp + lo, len * 2,
-                               hipMemcpyHostToDevice, up);
-        }
+        std::vector<std::thread> pool;
+        for (int t = 1; t < nt; ++t) pool.emplace_back(worker, t);
+        worker(0);
+        for (auto& th : pool) th.join();
+        e = (hipError_t)err.load();
     }
     if (up) {
         const hipError_t e2 = hipStreamSynchronize(up);
