@@ -968,7 +968,7 @@ int grid_for_tiles(int64_t ntiles, int cap) {
 // still launch kFillBlocks blocks, and grows when the blocks would outnumber
 // the state's per-block partial sums (ZERO_MAX_PARTIALS).
 constexpr int64_t kRunSteps = 16;
-constexpr int64_t kFillBlocks = 2048;
+constexpr int64_t kFillBlocks = 4096;
 template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
 void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
     const int64_t ntiles = (a.n + 256 * TU - 1) / (256 * TU);

@@ -4,14 +4,14 @@ of several tiles: whole outputs compared element by element with the oracle
 steps of one tile and one buffer group each, fewer when the shard is small),
 so these sizes reach, per case:
 
-  8 fp16 buffers, 30,000,123 elements   one group, R = 7 (odd step count)
-  32 bf16 buffers, 10,000,001           two groups of 16, R = 4 (8 steps)
-  12 fp16 buffers, 10,000,007, 2 micro-steps accumulated
+  8 fp16 buffers, 60,500,123 elements   one group, R = 7 (odd step count)
+  32 bf16 buffers, 10,000,257           two groups of 16, R = 2 (4 steps)
+  12 fp16 buffers, 20,000,263, 2 micro-steps accumulated
                                         three groups, R = 2 (6 steps)
-  8 INT8 payloads, 25,000,000           one group, R = 5
-  4 fp16 buffers, 70,000,000            one group, R = 16 (the full run)
-  2 fp32 buffers, 26,000,003            one group of two, R = 3
-  statistics pass, 40,000,001 fp16      one buffer, R = 9
+  8 INT8 payloads, 45,200,000           one group, R = 5
+  4 fp16 buffers, 135,000,000           one group, R = 16 (the full run)
+  2 fp32 buffers, 53,000,003            one group of two, R = 3
+  statistics pass, 80,000,001 fp16      one buffer, R = 9
 
 and in each the last wave's run is cut short by the end of the full tiles,
 followed by the ragged tail.  Bar: the reduced (or accumulated) shard bit for
@@ -62,8 +62,8 @@ def check_stats(state, red, scale):
 
 
 @pytest.mark.parametrize("dt,N,op,S,off", [
-    (1, 8, 1, 30_000_123, 8), (2, 32, 0, 10_000_001, 0), (1, 4, 1, 70_000_000, 0),
-    (0, 2, 0, 26_000_003, 4)])
+    (1, 8, 1, 60_500_123, 8), (2, 32, 0, 10_000_257, 0), (1, 4, 1, 135_000_000, 0),
+    (0, 2, 0, 53_000_003, 4)])
 def test_reduce_runs_whole_output(zf, dt, N, op, S, off):
     say("reduce runs", dt, N, op, S, off)
     bufs = inputs("red-%d-%d" % (dt, N), dt, N, off + S + 3)
@@ -76,7 +76,7 @@ def test_reduce_runs_whole_output(zf, dt, N, op, S, off):
 
 
 def test_accumulate_runs_whole_output(zf):
-    dt, N, op, S, off = 1, 12, 1, 10_000_007, 12
+    dt, N, op, S, off = 1, 12, 1, 20_000_263, 12
     say("accumulate runs", dt, N, op, S, off)
     acc_d = torch.zeros(S, device="cuda")
     acc = np.zeros(S, np.float32)
@@ -91,7 +91,7 @@ def test_accumulate_runs_whole_output(zf):
 
 
 def test_int8_reduce_runs_whole_output(zf):
-    N, S, block, op = 8, 25_000_000, 256, 1
+    N, S, block, op = 8, 45_200_000, 256, 1
     say("int8 reduce runs", N, S)
     nb = -(-S // block)
     qs = [synth.codes(synth.stream_key("runs", "q", k), 0, S) for k in range(N)]
@@ -108,7 +108,7 @@ def test_int8_reduce_runs_whole_output(zf):
 
 
 def test_statistics_pass_runs(zf):
-    dt, S = 1, 40_000_001
+    dt, S = 1, 80_000_001
     say("statistics runs", S)
     g = inputs("stats", dt, 1, S)[0]
     state = zf.StepState(65536.0, False)
