@@ -72,8 +72,8 @@ def parse():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="accepted for older command lines: the plain copy kernel (the counter "
-                         "calibration and the copy ceiling) now always runs")
+                    help="accepted for older command lines: the calibration kernels (the "
+                         "counters' copy reference and the ceilings) now always run")
     return ap.parse_args()
 
 
@@ -173,6 +173,18 @@ def run_prereduced(zf, torch, w, steps, warmup):
     st = opt.state.read()
     assert st.last_skipped == 0 and st.step == warmup + steps, "unexpected skipped step"
     res = dict(wall=wall, adam_ms=adam_ms, norm=st.last_norm)
+    # after the timed steps: the update's byte mix with trivial arithmetic on
+    # these same arrays (same physical placement), the kernel's own ceiling
+    n = S // 1024 * 1024
+    slot = ag[w.start:w.start + n]
+    from synth import synth as _s
+    mix_ms = _event_ms(torch, lambda: _s.mix28(grads[0][:n], opt.master[:n], opt.exp_avg[:n],
+                                               opt.exp_avg_sq[:n], slot), 5)
+    res["mix"] = dict(bytes_per_launch=28 * n, ms_per_launch=mix_ms,
+                      GBps=28 * n / (mix_ms * 1e-3) / 1e9,
+                      what="the update's byte mix (fp16 g, fp32 p/m/v, fp16 copy of p; trivial "
+                           "arithmetic, same lane layout) on the step's own arrays, after the "
+                           "timed steps")
     del opt, grads, ag, master
     torch.cuda.empty_cache()
     return res
@@ -441,32 +453,43 @@ def run_offload(zf, torch, w, steps, warmup):
                     % threads}
 
 
-def run_copy_calibration(torch, nbytes=4 << 30, reps=5):
-    """The plain streaming copy (synth copy16: 4 GiB read + 4 GiB written per
-    launch), timed with HIP events on the launch stream: the practical
-    read+write ceiling of this machine, measured in the same process as the step.
-    Its dispatches also calibrate the rocprofv3 byte counters."""
-    from synth import synth
-    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    src.fill_(1.0)
-    torch.cuda.synchronize()
+def _event_ms(torch, fn, reps):
     ms = []
     for _ in range(reps + 1):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        synth.copy(src, dst)
+        fn()
         e1.record()
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
     ms = sorted(ms[1:])
-    med = ms[len(ms) // 2]
-    del src, dst
+    return ms[len(ms) // 2]
+
+
+def run_ceilings(torch, nbytes=4 << 30, reps=5):
+    """The practical HBM ceilings of this machine, measured in the same process as
+    the step with the streaming calibration kernels of synth (non-temporal
+    16-byte accesses, HIP events on the launch stream): read-only, write-only
+    and copy (its dispatches also calibrate the rocprofv3 byte counters).  The
+    fused update's own byte mix is measured by run_prereduced on its arrays."""
+    from synth import synth
+    out = {}
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for name, fn, moved in (("read", lambda: synth.read_stream(a, sink), nbytes),
+                            ("write", lambda: synth.write_stream(b), nbytes),
+                            ("copy", lambda: synth.copy(a, b), 2 * nbytes)):
+        ms = _event_ms(torch, fn, reps)
+        out[name] = dict(bytes_per_launch=moved, ms_per_launch=ms, GBps=moved / (ms * 1e-3) / 1e9)
+    del a, b
     torch.cuda.empty_cache()
-    return dict(kernel="synth copy16 (non-temporal 16-byte copy, 16 KiB per block)",
-                bytes_per_launch=2 * nbytes,
-                ms_per_launch=med, GBps=2 * nbytes / (med * 1e-3) / 1e9)
+    out["what"] = ("synth calibration kernels, same process, read/write/copy over %d MiB; adamw_mix "
+                   "runs on the step's own arrays" % (nbytes >> 20))
+    return out
 
 
 def main():
@@ -483,8 +506,9 @@ def main():
     w = WORKLOADS["10b_n8"]
     S = w.shard
 
-    copy = run_copy_calibration(torch)
+    ceilings = run_ceilings(torch)
     res = run_prereduced(zf, torch, w, args.steps, args.warmup)
+    ceilings["adamw_mix"] = res["mix"]
     ms_step = res["wall"] / args.steps * 1e3
     adam_ms = sum(res["adam_ms"]) / len(res["adam_ms"])
     adam_bytes = ADAM_BYTES_PER_PARAM["f16"] * S
@@ -516,8 +540,9 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": read_traffic(),
                      "algorithmic_bytes_per_launch": adam_bytes,
                      "avg_launch_ms": adam_ms,
-                     "frac_of_copy_ceiling": achieved / copy["GBps"]},
-        "copy_ceiling": copy,
+                     "frac_of_copy_ceiling": achieved / ceilings["copy"]["GBps"],
+                     "frac_of_mix_ceiling": achieved / ceilings["adamw_mix"]["GBps"]},
+        "ceilings": ceilings,
     }
     if not args.no_variants:
         out["variants"] = {}

@@ -78,6 +78,12 @@ def _gpu_lib():
         L.synth_fill_codes.argtypes = [C.c_uint64, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
         L.synth_copy.restype = C.c_int
         L.synth_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
+        L.synth_read.restype = C.c_int
+        L.synth_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+        L.synth_write.restype = C.c_int
+        L.synth_write.argtypes = [C.c_void_p, C.c_int64, C.c_uint32, C.c_void_p]
+        L.synth_mix28.restype = C.c_int
+        L.synth_mix28.argtypes = [C.c_void_p] * 5 + [C.c_int64, C.c_void_p]
         _gpu = L
     return _gpu
 
@@ -187,3 +193,35 @@ def copy(src, dst, grid=0, stream=None):
                                grid, C.c_void_p(s))
     if rc != 0:
         raise RuntimeError("synth_copy failed: hip error %d" % rc)
+
+
+def _stream(stream):
+    import torch
+    return C.c_void_p(stream if stream is not None else torch.cuda.current_stream().cuda_stream)
+
+
+def read_stream(src, sink, stream=None):
+    """Read every byte of `src` once (calibration); `sink` is a 1-element int32 tensor."""
+    rc = _gpu_lib().synth_read(C.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                               C.c_void_p(sink.data_ptr()), _stream(stream))
+    if rc != 0:
+        raise RuntimeError("synth_read failed: hip error %d" % rc)
+
+
+def write_stream(dst, val=0x3f800000, stream=None):
+    """Write every byte of `dst` once (calibration)."""
+    rc = _gpu_lib().synth_write(C.c_void_p(dst.data_ptr()), dst.numel() * dst.element_size(), val,
+                                _stream(stream))
+    if rc != 0:
+        raise RuntimeError("synth_write failed: hip error %d" % rc)
+
+
+def mix28(g, p, m, v, lp, stream=None):
+    """The fused update's byte mix with trivial arithmetic (calibration): g and
+    lp 16-bit, p, m, v fp32, all of n elements, n a multiple of 1024."""
+    n = p.numel()
+    assert g.numel() == m.numel() == v.numel() == lp.numel() == n
+    rc = _gpu_lib().synth_mix28(*[C.c_void_p(t.data_ptr()) for t in (g, p, m, v, lp)], n,
+                                _stream(stream))
+    if rc != 0:
+        raise RuntimeError("synth_mix28 failed: hip error %d" % rc)

@@ -1,7 +1,9 @@
 /*
- * synth_gpu.hip -- seeded synthetic inputs on the GPU, plus the plain copy
- * kernel used to calibrate HBM traffic counters and the practical copy
- * ceiling.  Holds none of the optimizer step's arithmetic.
+ * synth_gpu.hip -- seeded synthetic inputs on the GPU, plus the streaming
+ * calibration kernels (copy, read-only, write-only, and the byte mix of a
+ * fused AdamW update with trivial arithmetic) that measure the practical HBM
+ * ceilings beside the step and calibrate the traffic counters.  Holds none of
+ * the optimizer step's arithmetic.
  *
  * The generator is the same definition as synth_cpu.c, implemented
  * independently here:
@@ -104,6 +106,75 @@ __global__ void __launch_bounds__(256) copy16(const u32x4* __restrict__ src,
     }
 }
 
+/* Read-only stream of 16-byte words (non-temporal), 16 KiB per block and
+ * pass; the XOR of the words is stored only if it equals `never`, which keeps
+ * the loads live. */
+__global__ void __launch_bounds__(256) read16(const u32x4* __restrict__ src, int64_t n16,
+                                              uint32_t never, uint32_t* __restrict__ sink) {
+    uint32_t x = 0;
+    for (int64_t b = (int64_t)blockIdx.x * 1024; b < n16; b += (int64_t)gridDim.x * 1024) {
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t i = b + 256 * k + threadIdx.x;
+            v[k] = i < n16 ? __builtin_nontemporal_load(src + i) : (u32x4)(0u);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+    if (x == never) sink[0] = x;
+}
+
+/* Write-only stream of 16-byte words (non-temporal), 16 KiB per block and pass. */
+__global__ void __launch_bounds__(256) write16(u32x4* __restrict__ dst, int64_t n16, uint32_t val) {
+    for (int64_t b = (int64_t)blockIdx.x * 1024; b < n16; b += (int64_t)gridDim.x * 1024) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t i = b + 256 * k + threadIdx.x;
+            if (i < n16) __builtin_nontemporal_store((u32x4)(val), dst + i);
+        }
+    }
+}
+
+/* The byte mix of the fused update with trivial arithmetic: per element a
+ * 16-bit g and fp32 p, m, v are read, p, m, v and a 16-bit copy of p are
+ * written (14 B in, 14 B out), in the update's layout (one 1024-element tile
+ * per wave; in slice u lane l holds elements 256u + 4l .. 4l+3) with
+ * non-temporal accesses.  ntiles full tiles, one per wave. */
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__global__ void __launch_bounds__(256) mix28(const uint16_t* __restrict__ g, float* __restrict__ p,
+                                             float* __restrict__ m, float* __restrict__ v,
+                                             uint16_t* __restrict__ lp, int64_t ntiles) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntiles) return;
+    u32x2 gw[4];
+    f32x4 pv[4], mv[4], vv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i0 = t * 1024 + 256 * u + 4 * lane;
+        gw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(g + i0));
+        pv[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + i0));
+        mv[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m + i0));
+        vv[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(v + i0));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i0 = t * 1024 + 256 * u + 4 * lane;
+        const float gf = (float)(gw[u].x & 0xffffu);
+        f32x4 a = pv[u], b = mv[u], c = vv[u];
+        a.x = a.x + gf; b.x = b.x + gf; c.x = c.x + gf;
+        __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p + i0));
+        __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(m + i0));
+        __builtin_nontemporal_store(c, reinterpret_cast<f32x4*>(v + i0));
+        u32x2 o;
+        o.x = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xffff0000u);
+        o.y = (__float_as_uint(a.z) >> 16) | (__float_as_uint(a.w) & 0xffff0000u);
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(lp + i0));
+    }
+}
+
 int grid_for(int64_t n) {
     int64_t g = (n + 255) / 256;
     if (g > 8192) g = 8192;
@@ -154,6 +225,46 @@ int synth_copy(const void* src, void* dst, int64_t nbytes, int32_t grid, void* s
     const int g = grid > 0 ? grid : (int)spans;
     hipLaunchKernelGGL(copy16, dim3(g), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
                        (u32x4*)dst, n16);
+    return (int)hipGetLastError();
+}
+
+/* Read-only stream over nbytes (a multiple of 16, 16-byte aligned); sink:
+ * one writable uint32. */
+int synth_read(const void* src, int64_t nbytes, void* sink, void* stream) {
+    if (nbytes <= 0) return 0;
+    if ((nbytes & 15) || ((uintptr_t)src & 15)) return (int)hipErrorInvalidValue;
+    const int64_t n16 = nbytes / 16;
+    int64_t spans = (n16 + 1023) / 1024;
+    if (spans > (1 << 22)) spans = 1 << 22;
+    hipLaunchKernelGGL(read16, dim3((int)spans), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4*)src, n16, 0x9e3779b9u, (uint32_t*)sink);
+    return (int)hipGetLastError();
+}
+
+/* Write-only stream over nbytes (a multiple of 16, 16-byte aligned). */
+int synth_write(void* dst, int64_t nbytes, uint32_t val, void* stream) {
+    if (nbytes <= 0) return 0;
+    if ((nbytes & 15) || ((uintptr_t)dst & 15)) return (int)hipErrorInvalidValue;
+    const int64_t n16 = nbytes / 16;
+    int64_t spans = (n16 + 1023) / 1024;
+    if (spans > (1 << 22)) spans = 1 << 22;
+    hipLaunchKernelGGL(write16, dim3((int)spans), dim3(256), 0, (hipStream_t)stream, (u32x4*)dst,
+                       n16, val);
+    return (int)hipGetLastError();
+}
+
+/* The fused update's byte mix over n elements (n a multiple of 1024; p, m, v
+ * 16-byte and g, lp 8-byte aligned). */
+int synth_mix28(const void* g, float* p, float* m, float* v, void* lp, int64_t n, void* stream) {
+    if (n <= 0) return 0;
+    if ((n & 1023) || ((uintptr_t)g & 7) || ((uintptr_t)lp & 7) || ((uintptr_t)p & 15) ||
+        ((uintptr_t)m & 15) || ((uintptr_t)v & 15))
+        return (int)hipErrorInvalidValue;
+    const int64_t ntiles = n / 1024;
+    const int64_t blocks = (ntiles + 3) / 4;
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mix28, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const uint16_t*)g, p, m, v, (uint16_t*)lp, ntiles);
     return (int)hipGetLastError();
 }
 
