@@ -182,7 +182,7 @@ int zero_step_state_init(zero_step_state_t* host_state, float loss_scale, int32_
  * the reduction runs in fp32.  For i in [0, shard_numel):
  *     acc = 0; for k = 0..n_ranks-1 (rank order): acc += f32(grad_bufs[k][elem_offset + i])
  *     red_out[i] = (op == ZERO_AVG) ? acc / n_ranks : acc          (fp32, IEEE)
- * grad_bufs: HOST array of n_ranks DEVICE pointers, each fp16 or bf16
+ * grad_bufs: HOST array of n_ranks DEVICE pointers, each fp16, bf16 or fp32
  *   (in_dtype), each valid over [elem_offset, elem_offset + shard_numel) --
  *   full padded flat buffers with elem_offset = r*S, or per-rank slices with
  *   elem_offset = 0.  1 <= n_ranks <= ZERO_MAX_RANKS.
