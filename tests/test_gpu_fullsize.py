@@ -295,3 +295,45 @@ def test_gpt1p5b_n64_rank0_full_size(zf):
     assert st.loss_scale == 65536.0 and st.step == w.steps and st.good_steps == w.steps
     del opt, ag, slices, master
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ 10B over 8 ranks, raw slices
+def test_10b_n8_reduce8_full_size(zf):
+    """The 8 raw fp16 rank slices of the 10B shard reduced (AVG) in the step,
+    with the statistics fused into the reduce, as the benchmark runs it: two
+    steps, the first with the norm recomputed over the whole shard."""
+    w = WORKLOADS["10b_n8_reduce8"]
+    S, start, N = w.shard, w.start, w.n_ranks
+    say("10b_n8_reduce8: shard", S, "ranks", N)
+    dev = torch.device("cuda:0")
+    master = torch.empty(S, device=dev)
+    synth.fill_normal(master, key_master(w), start, w.master_sigma)
+    opt = zf.ShardOptimizer(master, w.hp, loss_scale=w.loss_scale, dynamic=w.dynamic)
+    ag = torch.zeros(w.padded, dtype=torch.float16, device=dev)
+    slices = [torch.empty(S, dtype=torch.float16, device=dev) for _ in range(N)]
+    idx = sample_indices(S, 20_000, seed=5)
+    ref = OracleRank(master_at(w, start + idx), w.loss_scale, w.dynamic)
+    assert coef_is_one_by_bound(w, S, w.loss_scale)
+    for step in range(2):
+        say("10b_n8_reduce8 step", step)
+        for k in range(N):
+            synth.fill_normal(slices[k], key_grad(w, step, k), start, w.grad_sigma)
+        opt.step_from_rank_buffers(slices, 0, ag, start)
+        st = opt.state.read()
+        if step == 0:
+            sumsq, ovf = full_sumsq_reduce(w, step, w.loss_scale, chunk=1 << 22)
+            assert ovf == 0 and abs(st.last_norm - math.sqrt(sumsq)) <= 1e-5 * math.sqrt(sumsq)
+        else:
+            sumsq, ovf = 0.0, 0   # enters only through coef, fixed at 1 by the bound
+        hb = [rank_grad_at(w, step, k, start + idx) for k in range(N)]
+        red = orc.reduce(hb, w.grad_dtype, 0, idx.size, w.op)
+        assert_bitwise(gather(opt.reduced_buffer(), idx), red, "reduced shard step %d" % step)
+        res = ref.step(red, orc.F32, w.hp, w.param_dtype, sumsq_local=sumsq, overflow_local=ovf)
+        assert res["coef"] == 1.0 == st.last_coef and st.last_skipped == 0
+        assert_bitwise(gather(opt.master, idx), ref.p, "master step %d" % step)
+        assert_bitwise(gather(opt.exp_avg, idx), ref.m, "exp_avg step %d" % step)
+        assert_bitwise(gather(opt.exp_avg_sq, idx), ref.v, "exp_avg_sq step %d" % step)
+        assert_bitwise(gather(ag, start + idx), res["lp"], "slot step %d" % step)
+    assert st.step == 2
+    del opt, ag, slices, master
+    torch.cuda.empty_cache()
