@@ -220,7 +220,6 @@ int zero_unscale_norm(const void* grad_shard, int32_t dtype, int64_t n, zero_ste
     if (!grad_shard) return fail(ZERO_EINVAL, "zero_unscale_norm: grad_shard is NULL");
     if (!aligned(grad_shard, esize(dtype))) return fail(ZERO_EALIGN, "zero_unscale_norm: grad misaligned");
     if (!aligned(d_state, 8)) return fail(ZERO_EALIGN, "zero_unscale_norm: state not 8-byte aligned");
-    if (n == 0) return ok();
     zf::ReduceLaunch a;
     memset(&a, 0, sizeof a);
     a.bufs[0] = grad_shard;
