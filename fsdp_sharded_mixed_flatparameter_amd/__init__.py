@@ -280,6 +280,8 @@ def zero_adamw_shard_step(grad_shard, master, exp_avg, exp_avg_sq, allgather_buf
         _dev(t, name, ("float32",))
     _dev(allgather_buf, "allgather_buf", _F16_BF16)
     if q_buf is not None:
+        if q_scales is None:
+            raise ValueError("q_buf needs q_scales")
         _dev(q_buf, "q_buf", ("int8",))
         _dev(q_scales, "q_scales", ("float32",))
     if grad_shard.numel() < n or exp_avg.numel() != n or exp_avg_sq.numel() != n:
@@ -311,8 +313,6 @@ def zero_quant_allgather_slot(slot, q_buf, q_scales, q_slot_offset=0, q_scale_of
     _check(_lib.zero_quant_allgather_slot(_ptr(slot), _dtype_code(slot), n, block, _ptr(q_buf),
                                           q_slot_offset, _ptr(q_scales), q_scale_offset,
                                           _stream(stream)))
-
-
 
 
 def zero_grad_reduce_shard_int8(q_slices, scale_slices, shard_numel, op, red_out, state=None,

@@ -425,6 +425,13 @@ int zero_offload_step(const void* d_grad, int32_t grad_dtype, int64_t n, float* 
                   !aligned(h_exp_avg, 4) || !aligned(h_exp_avg_sq, 4) || !aligned(h_lp_stage, 2) ||
                   !aligned(d_allgather, 2)))
         return fail(ZERO_EALIGN, "%s: a buffer is not aligned to its element size", fn);
+    if (n > 0) {
+        // the chunks of one buffer are filled while other chunks of the other
+        // are read, so the two staging buffers must be disjoint
+        const uintptr_t g0 = reinterpret_cast<uintptr_t>(h_grad_stage), g1 = g0 + (uintptr_t)n * es;
+        const uintptr_t l0 = reinterpret_cast<uintptr_t>(h_lp_stage), l1 = l0 + (uintptr_t)n * 2;
+        if (g0 < l1 && l0 < g1) return fail(ZERO_EINVAL, "%s: the two staging buffers overlap", fn);
+    }
     zf::OffloadLaunch a;
     memset(&a, 0, sizeof a);
     a.d_grad = d_grad;

@@ -113,15 +113,19 @@ class OffloadShardOptimizer:
     def numel(self):
         return self.master.numel()
 
-    def _staging(self, dtype):
-        if dtype not in self._stage:
-            self._stage[dtype] = torch.empty(self.numel, dtype=dtype, pin_memory=True)
-        return self._stage[dtype]
+    def _staging(self, role, dtype):
+        """The pinned buffer for one direction ("grad" down, "param" up); the two
+        are never the same memory, also when both are 16-bit of one format."""
+        key = (role, dtype)
+        if key not in self._stage:
+            self._stage[key] = torch.empty(self.numel, dtype=dtype, pin_memory=True)
+        return self._stage[key]
 
     def step_from_reduced(self, grad_shard, allgather_buf, slot_offset, stream=None):
         """Statistics over the device gradient shard, then the offloaded step."""
         zero_unscale_norm(grad_shard, self.state, n=self.numel, stream=stream)
         zero_offload_step(grad_shard, self.master, self.exp_avg, self.exp_avg_sq,
-                          self._staging(grad_shard.dtype), self._staging(allgather_buf.dtype),
+                          self._staging("grad", grad_shard.dtype),
+                          self._staging("param", allgather_buf.dtype),
                           allgather_buf, slot_offset, self.hp, self.state, chunk=self.chunk,
                           n_threads=self.n_threads, stream=stream)

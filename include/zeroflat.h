@@ -379,7 +379,8 @@ int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const*
  *   its 16-bit parameters go to the PINNED h_lp_stage[n] and from there to the
  *   DEVICE All-Gather slot d_allgather[slot_offset ...] while later chunks are
  *   computed; finally the loss scaler / counters of d_state are updated on the
- *   device as by ZERO_STEP_FINALIZE.  Unlike the sections above this call
+ *   device as by ZERO_STEP_FINALIZE.  The two staging buffers must not
+ *   overlap (ZERO_EINVAL).  Unlike the sections above this call
  *   synchronizes: it returns after every copy and the finalize completed.  It
  *   creates and destroys its own HIP events and host threads, and allocates no
  *   device memory.  chunk 0 selects 2^24 elements.

@@ -199,3 +199,30 @@ def test_int8_gradient_reduce_validates_before_launch(zf):
     nul = (C.c_void_p * 2)(0x1000, 0)
     assert L.zero_grad_reduce_shard_int8(nul, s, 2, 8, 256, 1, p, None, None) == -1
     assert L.zero_grad_reduce_shard_int8(q, s, 2, 0, 256, 1, p, None, None) == 0
+
+
+def test_offload_step_validates_before_launch(zf):
+    """zero_offload_step rejects bad arguments, overlapping staging buffers
+    among them, before any copy or launch."""
+    L = zf.lib()
+    p = C.c_void_p(0x1000)
+    st = C.c_void_p(0x8000)
+    hp = zf.zero_adamw_hparams_t(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                                 max_grad_norm=1.0)
+
+    def call(grad_stage=0x20000, lp_stage=0x40000, n=1024, gdt=1, pdt=1, state=st, chunk=0):
+        return L.zero_offload_step(p, gdt, n, p, p, p, C.c_void_p(grad_stage),
+                                   C.c_void_p(lp_stage), p, pdt, 0, C.byref(hp), state, chunk, 0,
+                                   None)
+
+    assert call(state=None) == -1
+    assert call(state=C.c_void_p(0x8004)) == -2
+    assert call(gdt=5) == -1
+    assert call(pdt=0) == -1                                   # fp32 parameters
+    assert call(n=-1) == -1
+    assert call(chunk=-5) == -1
+    assert call(grad_stage=0x20001) == -2
+    assert call(lp_stage=0x20000) == -1                        # the same buffer
+    assert b"overlap" in L.zero_last_error()
+    assert call(grad_stage=0x20000, lp_stage=0x20000 + 2 * 1024 - 2) == -1   # last element shared
+    assert call(gdt=0, grad_stage=0x20000, lp_stage=0x20000 + 2 * 1024) == -1  # fp32 grads: 4 B each
