@@ -185,6 +185,14 @@ def run_prereduced(zf, torch, w, steps, warmup):
                       what="the update's byte mix (fp16 g, fp32 p/m/v, fp16 copy of p; trivial "
                            "arithmetic, same lane layout) on the step's own arrays, after the "
                            "timed steps")
+    # and a plain copy between two of them (master into exp_avg; the state is
+    # not used again): every streaming kernel on these arrays moves with their
+    # physical placement, so this is the ceiling the update is compared with
+    copy_ms = _event_ms(torch, lambda: _s.copy(opt.master, opt.exp_avg), 5)
+    res["copy"] = dict(bytes_per_launch=8 * S, ms_per_launch=copy_ms,
+                       GBps=8 * S / (copy_ms * 1e-3) / 1e9,
+                       what="plain non-temporal 16-byte copy of the fp32 master into exp_avg "
+                            "(the step's own arrays), after the timed steps")
     del opt, grads, ag, master
     torch.cuda.empty_cache()
     return res
@@ -436,7 +444,7 @@ def run_offload(zf, torch, w, steps, warmup):
     st = opt.state.read()
     assert st.last_skipped == 0 and st.step == warmup + steps
     # the host update alone (no copies), same threads, same arrays
-    stage = opt._staging(torch.float16)
+    stage = opt._staging("grad", torch.float16)
     lp_out = torch.empty(S, dtype=torch.float16)
     best = 1e30
     for _ in range(2):
@@ -537,6 +545,7 @@ def main():
     ceilings = run_ceilings(torch)
     res = run_prereduced(zf, torch, w, args.steps, args.warmup)
     ceilings["adamw_mix"] = res["mix"]
+    ceilings["copy_step_arrays"] = res["copy"]
     ms_step = res["wall"] / args.steps * 1e3
     adam_ms = sum(res["adam_ms"]) / len(res["adam_ms"])
     adam_bytes = ADAM_BYTES_PER_PARAM["f16"] * S
@@ -569,7 +578,8 @@ def main():
                      "algorithmic_bytes_per_launch": adam_bytes,
                      "avg_launch_ms": adam_ms,
                      "frac_of_copy_ceiling": achieved / ceilings["copy"]["GBps"],
-                     "frac_of_mix_ceiling": achieved / ceilings["adamw_mix"]["GBps"]},
+                     "frac_of_mix_ceiling": achieved / ceilings["adamw_mix"]["GBps"],
+                     "frac_of_step_array_copy": achieved / ceilings["copy_step_arrays"]["GBps"]},
         "ceilings": ceilings,
     }
     if not args.no_variants:
