@@ -380,6 +380,18 @@ int check_hp(const char* fn, const zero_adamw_hparams_t* hp) {
 }
 }  // namespace
 
+namespace {
+// The gradient array and the 16-bit parameter array of the host step: either
+// disjoint, or the very same array when the gradient is 16-bit too (in-place
+// staging, each element's gradient read before its parameter is stored).
+bool staging_ok(const void* g, int gsize, const void* lp, int64_t n) {
+    if (g == lp) return gsize == 2;
+    const uintptr_t g0 = reinterpret_cast<uintptr_t>(g), g1 = g0 + (uintptr_t)n * gsize;
+    const uintptr_t l0 = reinterpret_cast<uintptr_t>(lp), l1 = l0 + (uintptr_t)n * 2;
+    return g1 <= l0 || l1 <= g0;
+}
+}  // namespace
+
 int zero_offload_adamw_host(const void* grad, int32_t grad_dtype, float* master, float* exp_avg,
                             float* exp_avg_sq, int64_t n, void* lp_out, int32_t param_dtype,
                             const zero_adamw_hparams_t* hp, const zero_step_state_t* host_state,
@@ -396,6 +408,8 @@ int zero_offload_adamw_host(const void* grad, int32_t grad_dtype, float* master,
     if (n > 0 && (!aligned(grad, esize(grad_dtype)) || !aligned(master, 4) || !aligned(exp_avg, 4) ||
                   !aligned(exp_avg_sq, 4) || !aligned(lp_out, 2)))
         return fail(ZERO_EALIGN, "%s: an array is not aligned to its element size", fn);
+    if (n > 0 && !staging_ok(grad, esize(grad_dtype), lp_out, n))
+        return fail(ZERO_EINVAL, "%s: lp_out overlaps grad other than as the same 16-bit array", fn);
     int sk = 0;
     zf::offload_adam_host(grad, grad_dtype, master, exp_avg, exp_avg_sq, n, lp_out, param_dtype, *hp,
                           *host_state, n_threads, &sk);
@@ -425,13 +439,10 @@ int zero_offload_step(const void* d_grad, int32_t grad_dtype, int64_t n, float* 
                   !aligned(h_exp_avg, 4) || !aligned(h_exp_avg_sq, 4) || !aligned(h_lp_stage, 2) ||
                   !aligned(d_allgather, 2)))
         return fail(ZERO_EALIGN, "%s: a buffer is not aligned to its element size", fn);
-    if (n > 0) {
-        // the chunks of one buffer are filled while other chunks of the other
-        // are read, so the two staging buffers must be disjoint
-        const uintptr_t g0 = reinterpret_cast<uintptr_t>(h_grad_stage), g1 = g0 + (uintptr_t)n * es;
-        const uintptr_t l0 = reinterpret_cast<uintptr_t>(h_lp_stage), l1 = l0 + (uintptr_t)n * 2;
-        if (g0 < l1 && l0 < g1) return fail(ZERO_EINVAL, "%s: the two staging buffers overlap", fn);
-    }
+    // chunks of one buffer are filled while other chunks of the other are
+    // read: the two are disjoint, or one 16-bit buffer used in place
+    if (n > 0 && !staging_ok(h_grad_stage, es, h_lp_stage, n))
+        return fail(ZERO_EINVAL, "%s: the staging buffers overlap other than as one 16-bit buffer", fn);
     zf::OffloadLaunch a;
     memset(&a, 0, sizeof a);
     a.d_grad = d_grad;

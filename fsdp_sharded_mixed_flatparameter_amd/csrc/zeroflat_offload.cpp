@@ -95,25 +95,38 @@ inline float grad_at(const void* g, int64_t i) {
     else return b2f(static_cast<const uint16_t*>(g)[i]);
 }
 
+// g and lp may be the same 16-bit array (in-place staging: the chunk's
+// gradients are overwritten by its parameters).  Each block of kHostBlock
+// elements first reads its gradients into a local array and only then
+// computes and stores, so every element's gradient is read before its slot is
+// written, and both loops still vectorize (p, m and v are restrict; the local
+// array cannot alias lp).
+constexpr int kHostBlock = 64;
+
 template <int GT, int PT>
-__attribute__((always_inline)) inline void adam_loop(const Scalars& s, const void* __restrict__ g,
+__attribute__((always_inline)) inline void adam_loop(const Scalars& s, const void* g,
                                                      float* __restrict__ p, float* __restrict__ m,
-                                                     float* __restrict__ v,
-                                                     uint16_t* __restrict__ lp, int64_t lo,
-                                                     int64_t hi) {
-    for (int64_t i = lo; i < hi; ++i) {
-        const float u = grad_at<GT>(g, i) * s.inv;   // unscale
-        const float gg = u * s.coef;                 // clip
-        const float mn = s.b1 * m[i] + s.c1 * gg;
-        const float vn = s.b2 * v[i] + s.c2 * (gg * gg);
-        const float mh = mn / s.bc1;
-        const float vh = vn / s.bc2;
-        const float d = __builtin_sqrtf(vh) + s.eps;
-        const float pn = p[i] * s.wdf - (s.lr * mh) / d;
-        p[i] = pn;
-        m[i] = mn;
-        v[i] = vn;
-        lp[i] = (uint16_t)(PT == ZERO_F16 ? f2h(pn) : f2b(pn));
+                                                     float* __restrict__ v, uint16_t* lp,
+                                                     int64_t lo, int64_t hi) {
+    for (int64_t i0 = lo; i0 < hi; i0 += kHostBlock) {
+        const int nb = hi - i0 < kHostBlock ? (int)(hi - i0) : kHostBlock;
+        float gb[kHostBlock];
+        for (int j = 0; j < nb; ++j) gb[j] = grad_at<GT>(g, i0 + j);
+        for (int j = 0; j < nb; ++j) {
+            const int64_t i = i0 + j;
+            const float u = gb[j] * s.inv;               // unscale
+            const float gg = u * s.coef;                 // clip
+            const float mn = s.b1 * m[i] + s.c1 * gg;
+            const float vn = s.b2 * v[i] + s.c2 * (gg * gg);
+            const float mh = mn / s.bc1;
+            const float vh = vn / s.bc2;
+            const float d = __builtin_sqrtf(vh) + s.eps;
+            const float pn = p[i] * s.wdf - (s.lr * mh) / d;
+            p[i] = pn;
+            m[i] = mn;
+            v[i] = vn;
+            lp[i] = (uint16_t)(PT == ZERO_F16 ? f2h(pn) : f2b(pn));
+        }
     }
 }
 

@@ -93,10 +93,12 @@ class OffloadShardOptimizer:
     """ZeRO-Offload for one rank's shard: the fp32 master, m and v live in host
     memory and the update runs on host cores; the device keeps the gradient
     shard, the step state and the All-Gather buffer.  Pinned staging buffers
-    carry the gradient to the host and the 16-bit parameters back."""
+    carry the gradient to the host and the 16-bit parameters back; with a
+    16-bit gradient and `in_place_staging`, one buffer serves both ways (each
+    chunk's parameters overwrite its gradients in place)."""
 
     def __init__(self, master_host, hp, loss_scale=65536.0, dynamic=False, window=1000,
-                 min_scale=1.0, device="cuda", n_threads=0, chunk=0):
+                 min_scale=1.0, device="cuda", n_threads=0, chunk=0, in_place_staging=True):
         if master_host.dtype != torch.float32 or master_host.is_cuda or \
                 not master_host.is_contiguous():
             raise ValueError("master must be a contiguous float32 host tensor")
@@ -107,6 +109,7 @@ class OffloadShardOptimizer:
         self.state = StepState(loss_scale, dynamic, window, min_scale, device=device)
         self.n_threads = n_threads
         self.chunk = chunk
+        self.in_place_staging = in_place_staging
         self._stage = {}
 
     @property
@@ -114,18 +117,22 @@ class OffloadShardOptimizer:
         return self.master.numel()
 
     def _staging(self, role, dtype):
-        """The pinned buffer for one direction ("grad" down, "param" up); the two
-        are never the same memory, also when both are 16-bit of one format."""
+        """The pinned buffer for one direction ("grad" down, "param" up)."""
         key = (role, dtype)
         if key not in self._stage:
             self._stage[key] = torch.empty(self.numel, dtype=dtype, pin_memory=True)
         return self._stage[key]
 
+    def _staging_pair(self, grad_dtype, param_dtype):
+        g = self._staging("grad", grad_dtype)
+        if self.in_place_staging and g.element_size() == 2:
+            return g, g.view(param_dtype)
+        return g, self._staging("param", param_dtype)
+
     def step_from_reduced(self, grad_shard, allgather_buf, slot_offset, stream=None):
         """Statistics over the device gradient shard, then the offloaded step."""
         zero_unscale_norm(grad_shard, self.state, n=self.numel, stream=stream)
-        zero_offload_step(grad_shard, self.master, self.exp_avg, self.exp_avg_sq,
-                          self._staging("grad", grad_shard.dtype),
-                          self._staging("param", allgather_buf.dtype),
+        g_stage, lp_stage = self._staging_pair(grad_shard.dtype, allgather_buf.dtype)
+        zero_offload_step(grad_shard, self.master, self.exp_avg, self.exp_avg_sq, g_stage, lp_stage,
                           allgather_buf, slot_offset, self.hp, self.state, chunk=self.chunk,
                           n_threads=self.n_threads, stream=stream)

@@ -368,8 +368,10 @@ int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const*
  *   exp_avg, exp_avg_sq fp32[n], lp_out[n] of param_dtype); host_state is a
  *   HOST copy of the step state after the statistics calls; nothing is
  *   written and *skipped = 1 if it records an overflow.  It does not update
- *   the loss scaler (see below).  n_threads host threads (0: every hardware
- *   thread).  Blocks until done; no HIP calls.
+ *   the loss scaler (see below).  lp_out may be grad itself when grad is
+ *   fp16/bf16 (each element's gradient is read before its parameter
+ *   overwrites it); any other overlap is refused (ZERO_EINVAL).  n_threads
+ *   host threads (0: every hardware thread).  Blocks until done; no HIP calls.
  * zero_offload_step: the whole offloaded step for a rank whose statistics
  *   (zero_grad_reduce_shard / zero_unscale_norm into d_state) are already
  *   enqueued on `stream`.  The DEVICE gradient shard d_grad[n] moves to the
@@ -379,8 +381,11 @@ int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const*
  *   its 16-bit parameters go to the PINNED h_lp_stage[n] and from there to the
  *   DEVICE All-Gather slot d_allgather[slot_offset ...] while later chunks are
  *   computed; finally the loss scaler / counters of d_state are updated on the
- *   device as by ZERO_STEP_FINALIZE.  The two staging buffers must not
- *   overlap (ZERO_EINVAL).  Unlike the sections above this call
+ *   device as by ZERO_STEP_FINALIZE.  With a 16-bit gradient the two
+ *   staging buffers may be one buffer (h_lp_stage == h_grad_stage): each
+ *   chunk's parameters then overwrite its gradients in place, which halves
+ *   the pinned memory; any other overlap is refused (ZERO_EINVAL).  Unlike
+ *   the sections above this call
  *   synchronizes: it returns after every copy and the finalize completed.  It
  *   creates and destroys its own HIP events and host threads, and allocates no
  *   device memory.  chunk 0 selects 2^24 elements.

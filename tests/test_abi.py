@@ -202,8 +202,9 @@ def test_int8_gradient_reduce_validates_before_launch(zf):
 
 
 def test_offload_step_validates_before_launch(zf):
-    """zero_offload_step rejects bad arguments, overlapping staging buffers
-    among them, before any copy or launch."""
+    """zero_offload_step rejects bad arguments before any copy or launch,
+    among them staging buffers that overlap other than as one 16-bit buffer
+    used in place."""
     L = zf.lib()
     p = C.c_void_p(0x1000)
     st = C.c_void_p(0x8000)
@@ -222,7 +223,8 @@ def test_offload_step_validates_before_launch(zf):
     assert call(n=-1) == -1
     assert call(chunk=-5) == -1
     assert call(grad_stage=0x20001) == -2
-    assert call(lp_stage=0x20000) == -1                        # the same buffer
+    assert call(gdt=0, lp_stage=0x20000) == -1                 # one buffer, fp32 gradient
     assert b"overlap" in L.zero_last_error()
+    assert call(lp_stage=0x20002) == -1                        # 16-bit, shifted by one element
     assert call(grad_stage=0x20000, lp_stage=0x20000 + 2 * 1024 - 2) == -1   # last element shared
     assert call(gdt=0, grad_stage=0x20000, lp_stage=0x20000 + 2 * 1024) == -1  # fp32 grads: 4 B each

@@ -75,6 +75,43 @@ def test_host_step_matches_oracle(zf, orc, gdt, pdt, n, threads, scale):
         assert np.array_equal(bits16(lp), lp_ref), step
 
 
+@pytest.mark.parametrize("gdt,pdt,n,threads", [(1, 1, 262_528, 4), (2, 1, 70_001, 3),
+                                              (1, 2, 4097, 16), (2, 2, 1, 1)])
+def test_host_step_in_place(zf, orc, gdt, pdt, n, threads):
+    """A 16-bit gradient and the 16-bit parameters in one array (in-place
+    staging): the parameters that overwrite the gradient, and master, m, v,
+    equal the oracle's bit for bit over three steps (the later ones clipped)."""
+    scale = 1024.0
+    p0 = synth.normal_f32(synth.stream_key("offload-inplace", gdt, pdt, n), 0, n, 0.02)
+    p_ref, m_ref, v_ref = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    p, m, v = host_tensor(p0, 0), torch.zeros(n), torch.zeros(n)
+    hp = orc.Hparams(**HP)
+    for step in range(3):
+        g = synth.normal(synth.stream_key("offload-inplace-g", gdt, n, step), 0, n, 1e-3, gdt)
+        sumsq, _ = orc.unscale_stats(g, gdt, scale)
+        remote = 0.0 if step == 0 else 4.0 * max(sumsq, 1e-30)
+        st = state_for(zf, step, scale, sumsq, remote)
+        buf = host_tensor(g, gdt)
+        assert zf.zero_offload_adamw_host(buf, p, m, v, buf.view(TDT[pdt]), HP, st, threads) == 0
+        coef = orc.clip_coef(sumsq + remote, HP["max_grad_norm"])
+        lp_ref = orc.adamw(g, gdt, p_ref, m_ref, v_ref, scale, coef, step + 1, hp, pdt)
+        for name, got, ref in (("master", p, p_ref), ("exp_avg", m, m_ref), ("exp_avg_sq", v, v_ref)):
+            assert np.array_equal(got.numpy().view(np.uint32), ref.view(np.uint32)), (name, step)
+        assert np.array_equal(bits16(buf), lp_ref), step
+
+
+def test_host_step_refuses_partial_overlap(zf):
+    n = 1000
+    st = state_for(zf, 0, 1.0)
+    p, m, v = torch.zeros(n), torch.zeros(n), torch.zeros(n)
+    big = torch.zeros(n + 1, dtype=torch.float16)
+    with pytest.raises(zf.ZeroError, match="overlaps"):
+        zf.zero_offload_adamw_host(big[:n], p, m, v, big[1:], HP, st)    # shifted by one
+    g32 = torch.zeros(n)
+    with pytest.raises(zf.ZeroError, match="overlaps"):
+        zf.zero_offload_adamw_host(g32, p, m, v, g32.view(torch.float16)[:n], HP, st)
+
+
 def test_host_step_skips_on_overflow(zf):
     n = 1000
     p = torch.randn(n)
