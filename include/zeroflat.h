@@ -45,8 +45,10 @@
  *     failure zero_last_error() returns a thread-local message.  Arguments are
  *     validated before anything is launched: on error nothing ran.
  *   - Device pointers are owned by the caller; the library never allocates
- *     or frees memory and never synchronizes.  It cannot see allocation
- *     sizes: the caller vouches that every range it names is allocated.
+ *     or frees device memory.  Except for the ZeRO-Offload step (section 8),
+ *     which runs on host threads and returns when done, no call allocates
+ *     host memory or synchronizes.  The library cannot see allocation sizes:
+ *     the caller vouches that every range it names is allocated.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); all
  *     kernels of a call are enqueued on it, in order.
  *   - Element counts and offsets are int64 (slot offsets exceed 2^31).
