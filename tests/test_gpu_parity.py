@@ -54,6 +54,8 @@ REDUCE_CASES = [
     (1, 3, 0, 1000, 3), (2, 8, 0, 100_000, 16), (2, 8, 1, 100_000, 16), (2, 8, 1, 9_999, 5),
     (2, 5, 1, 777, 0), (0, 4, 1, 3000, 4), (0, 2, 0, 3001, 1), (1, 1, 1, 2049, 0),
     (1, 11, 1, 4097, 0), (2, 17, 0, 5000, 8), (1, 16, 1, 5003, 0), (2, 48, 0, 3001, 8),
+    # the most buffers one call takes (ZERO_MAX_RANKS), and an odd count just below
+    (1, 256, 1, 3001, 0), (2, 255, 1, 1000, 2), (0, 256, 0, 2000, 4),
 ]
 
 
