@@ -43,6 +43,7 @@ ACC_CASES = [
     (1, 4, 1, 262_528, 262_528, 2), (2, 8, 0, 100_003, 16, 3), (1, 64, 1, 20_000, 0, 2),
     (0, 2, 1, 3001, 1, 2), (1, 3, 1, 1000, 3, 2), (2, 8, 1, 1, 0, 2), (1, 1, 0, 4097, 0, 4),
     (2, 5, 1, 2048 * 4, 8, 2),
+    (1, 256, 1, 2001, 0, 2), (2, 255, 0, 999, 4, 2),     # the most buffers per call, odd below
 ]
 
 

@@ -47,6 +47,7 @@ DEQ_CASES = [
     (4, 262_528, 256, 1, 0), (8, 2048 * 3 + 100, 256, 2, 0), (3, 1001, 256, 2, 0),
     (5, 4096 + 12, 64, 0, 0), (2, 3000, 12, 2, 0), (2, 2048, 256, 2, 1), (2, 4096, 4, 1, 0),
     (64, 20_000, 256, 2, 0), (7, 513, 256, 0, 0),
+    (65536, 4, 4, 2, 0), (65536, 7, 256, 1, 0),    # the most slots per call (tiny slots)
 ]
 
 
