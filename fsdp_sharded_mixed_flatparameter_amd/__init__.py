@@ -425,4 +425,4 @@ def unflatten(flat, shapes, n_ranks=1, align=1):
 
 
 from . import shard  # noqa: E402
-from .shard import OffloadShardOptimizer, ShardOptimizer  # noqa: E402,F401
+from .shard import MultiShardOptimizer, OffloadShardOptimizer, ShardOptimizer  # noqa: E402,F401

@@ -136,3 +136,63 @@ class OffloadShardOptimizer:
         zero_offload_step(grad_shard, self.master, self.exp_avg, self.exp_avg_sq, g_stage, lp_stage,
                           allgather_buf, slot_offset, self.hp, self.state, chunk=self.chunk,
                           n_threads=self.n_threads, stream=stream)
+
+
+class MultiShardOptimizer:
+    """One rank's shards of several FlatParameters (one per FSDP unit) under a
+    single optimizer.  One step state serves every unit, so the global gradient
+    norm, the clip coefficient, the overflow skip and the loss scale cover all
+    of them, as one optimizer over all the model's parameters does.  A step
+    takes the statistics of every unit first, then runs each unit's AdamW, and
+    updates the loss scaler once, after the last unit."""
+
+    def __init__(self, masters, hp, loss_scale=65536.0, dynamic=False, window=1000,
+                 min_scale=1.0):
+        if not masters:
+            raise ValueError("need at least one master shard")
+        for k, mst in enumerate(masters):
+            if mst.dtype != torch.float32 or not mst.is_cuda or not mst.is_contiguous():
+                raise ValueError("masters[%d] must be a contiguous float32 CUDA tensor" % k)
+        self.master = list(masters)
+        self.exp_avg = [torch.zeros_like(mst) for mst in masters]
+        self.exp_avg_sq = [torch.zeros_like(mst) for mst in masters]
+        self.hp = dict(hp)
+        self.state = StepState(loss_scale, dynamic, window, min_scale, device=masters[0].device)
+        self._red = [None] * len(masters)
+
+    def __len__(self):
+        return len(self.master)
+
+    def _check(self, *lists):
+        for x in lists:
+            if len(x) != len(self.master):
+                raise ValueError("one entry per unit expected (%d units)" % len(self.master))
+
+    def step_from_rank_buffers(self, grad_bufs, elem_offsets, allgather_bufs, slot_offsets,
+                               op=ZERO_AVG, stream=None):
+        """grad_bufs[u]: unit u's N rank gradient buffers; the reduce of each
+        unit with its statistics, then the step of every unit."""
+        self._check(grad_bufs, elem_offsets, allgather_bufs, slot_offsets)
+        reds = []
+        for u, (bufs, off) in enumerate(zip(grad_bufs, elem_offsets)):
+            if self._red[u] is None:
+                self._red[u] = torch.empty_like(self.master[u])
+            zero_grad_reduce_shard(bufs, off, self.master[u].numel(), op, self._red[u], self.state,
+                                   stream=stream)
+            reds.append(self._red[u])
+        self._apply(reds, allgather_bufs, slot_offsets, stream)
+
+    def step_from_reduced(self, grad_shards, allgather_bufs, slot_offsets, stream=None):
+        """Statistics over every unit's reduced (fp32/fp16/bf16) shard, then the
+        step of every unit."""
+        self._check(grad_shards, allgather_bufs, slot_offsets)
+        for u, g in enumerate(grad_shards):
+            zero_unscale_norm(g, self.state, n=self.master[u].numel(), stream=stream)
+        self._apply(grad_shards, allgather_bufs, slot_offsets, stream)
+
+    def _apply(self, grads, allgather_bufs, slot_offsets, stream):
+        last = len(grads) - 1
+        for u, g in enumerate(grads):
+            zero_adamw_shard_step(g, self.master[u], self.exp_avg[u], self.exp_avg_sq[u],
+                                  allgather_bufs[u], slot_offsets[u], self.hp, self.state,
+                                  finalize=u == last, stream=stream)
