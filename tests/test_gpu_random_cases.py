@@ -9,7 +9,10 @@ buffer inside its allocation (so pointers are 2-, 4-, 8- or 16-byte aligned
 and the vector and element-wise paths both run), accumulation into an fp32
 shard or a plain reduce, and whether the statistics are taken.  The
 quantiser, the INT8 consumer and the AdamW step get random lengths, offsets,
-formats, blocks and clipping the same way."""
+formats, blocks and clipping the same way.  ZF_RANDOM_SCALE=k in the
+environment draws k times as many seeds of every kind."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,6 +22,9 @@ from oracle import oracle as orc
 from synth import synth
 
 pytestmark = pytest.mark.gpu
+
+# ZF_RANDOM_SCALE=k draws k times as many seeds of every kind (default 1)
+SCALE = max(1, int(os.environ.get("ZF_RANDOM_SCALE", "1")))
 
 TORCH_DT = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}
 
@@ -66,7 +72,7 @@ def reduce_case(i):
     return N, dt, op, S, off, start, out_start, acc, stats, scale
 
 
-@pytest.mark.parametrize("i", range(60))
+@pytest.mark.parametrize("i", range(60 * SCALE))
 def test_random_reduce(zf, i):
     N, dt, op, S, off, start, out_start, acc, stats, scale = reduce_case(i)
     say("random reduce", i, dict(N=N, dt=dt, op=op, S=S, off=off, start=start, out_start=out_start,
@@ -94,7 +100,7 @@ def test_random_reduce(zf, i):
         assert rel(st.sumsq, s_ref) <= max(1e-12, S * 2.0 ** -53)
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(12 * SCALE))
 def test_random_int8_reduce(zf, i):
     r = np.random.default_rng(7300 + i)
     N = int(r.choice([1, 2, 3, 8, 16, 24, 64]))
@@ -120,7 +126,7 @@ def test_random_int8_reduce(zf, i):
     assert rel(st.sumsq, s_ref) <= max(1e-12, S * 2.0 ** -53)
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(16 * SCALE))
 def test_random_quantiser(zf, i):
     r = np.random.default_rng(7500 + i)
     pdt = int(r.integers(1, 3))
@@ -141,7 +147,7 @@ def test_random_quantiser(zf, i):
     assert_bitwise(to_host(s), rs, "scales")
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(12 * SCALE))
 def test_random_consumer(zf, i):
     r = np.random.default_rng(7700 + i)
     n_slots = int(r.integers(1, 10))
@@ -161,7 +167,7 @@ def test_random_consumer(zf, i):
     assert_bitwise(to_host(out), ref, "dequantised flat parameter")
 
 
-@pytest.mark.parametrize("i", range(10))
+@pytest.mark.parametrize("i", range(10 * SCALE))
 def test_random_adamw_steps(zf, i):
     import test_gpu_parity as parity
     r = np.random.default_rng(7900 + i)
