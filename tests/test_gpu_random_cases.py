@@ -181,3 +181,48 @@ def test_random_adamw_steps(zf, i):
     say("random adamw", i, dict(gdt=gdt, pdt=pdt, n=n, slot=slot, quant=quant, max_norm=max_norm,
                                 scale=scale))
     parity.test_adamw_step_parity(zf, gdt, pdt, n, slot, quant, max_norm, scale)
+
+
+@pytest.mark.parametrize("i", range(12 * SCALE))
+def test_random_offload(zf, i):
+    """The offloaded step (statistics on the GPU, the update on host threads,
+    chunked copies both ways) over a random size, chunk, thread count, pair of
+    formats and staging (in place or two buffers), two steps, the second
+    sometimes overflowing; master, m, v and the slot bit for bit."""
+    from harness import OracleRank
+    r = np.random.default_rng(8100 + i)
+    gdt = int(r.integers(0, 3))
+    pdt = int(r.integers(1, 3))
+    n = int(r.choice([1, 100, 4097, 65_536, 100_003, 300_001]))
+    chunk = max(int(r.choice([1, 1000, 4096, 65_536, 1 << 24])), -(-n // 64))   # <= 64 chunks
+    threads = int(r.integers(1, 17))
+    in_place = bool(r.integers(0, 2))
+    slot = int(r.integers(0, 9))
+    scale = 1024.0 if gdt != 2 else 1.0
+    overflow_step = int(r.integers(0, 3))          # 2: no overflow
+    say("random offload", i, dict(gdt=gdt, pdt=pdt, n=n, chunk=chunk, threads=threads,
+                                  in_place=in_place, slot=slot, overflow_step=overflow_step))
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=1.0)
+    p0 = synth.normal_f32(synth.stream_key("rnd-off-p", i), 0, n, 0.02)
+    opt = zf.OffloadShardOptimizer(torch.from_numpy(p0.copy()), hp, loss_scale=scale, dynamic=True,
+                                   window=1, n_threads=threads, chunk=chunk,
+                                   in_place_staging=in_place)
+    ref = OracleRank(p0, scale, True, window=1)
+    ag = torch.zeros(slot + n + 3, dtype=TORCH_DT[pdt], device="cuda")
+    for step in range(2):
+        g = synth.normal(synth.stream_key("rnd-off-g", i, step), 0, n, 1e-3 * scale, gdt)
+        if step == overflow_step:
+            g[n // 2] = np.float32(np.inf) if gdt == 0 else 0x7F80 if gdt == 2 else 0x7C00
+        opt.step_from_reduced(to_dev(g, gdt), ag, slot)
+        res = ref.step(g, gdt, hp, pdt)
+        st = opt.state.read()
+        assert st.last_skipped == res["skipped"] == int(step == overflow_step)
+        assert (st.loss_scale, st.good_steps, st.step) == \
+            (ref.scaler.loss_scale, ref.scaler.good_steps, ref.scaler.step)
+        assert_bitwise(opt.master.numpy(), ref.p, "master step %d" % step)
+        assert_bitwise(opt.exp_avg.numpy(), ref.m, "exp_avg step %d" % step)
+        assert_bitwise(opt.exp_avg_sq.numpy(), ref.v, "exp_avg_sq step %d" % step)
+        if not res["skipped"]:
+            assert st.last_coef == res["coef"]
+            assert_bitwise(to_host(ag[slot:slot + n]), res["lp"], "slot step %d" % step)
+    assert not to_host(ag[:slot]).any() and not to_host(ag[slot + n:]).any()
