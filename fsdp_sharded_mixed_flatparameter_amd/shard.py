@@ -168,19 +168,39 @@ class MultiShardOptimizer:
             if len(x) != len(self.master):
                 raise ValueError("one entry per unit expected (%d units)" % len(self.master))
 
+    def _reduced(self, u):
+        if self._red[u] is None:
+            self._red[u] = torch.empty_like(self.master[u])
+        return self._red[u]
+
     def step_from_rank_buffers(self, grad_bufs, elem_offsets, allgather_bufs, slot_offsets,
                                op=ZERO_AVG, stream=None):
         """grad_bufs[u]: unit u's N rank gradient buffers; the reduce of each
         unit with its statistics, then the step of every unit."""
         self._check(grad_bufs, elem_offsets, allgather_bufs, slot_offsets)
-        reds = []
         for u, (bufs, off) in enumerate(zip(grad_bufs, elem_offsets)):
-            if self._red[u] is None:
-                self._red[u] = torch.empty_like(self.master[u])
-            zero_grad_reduce_shard(bufs, off, self.master[u].numel(), op, self._red[u], self.state,
-                                   stream=stream)
-            reds.append(self._red[u])
-        self._apply(reds, allgather_bufs, slot_offsets, stream)
+            zero_grad_reduce_shard(bufs, off, self.master[u].numel(), op, self._reduced(u),
+                                   self.state, stream=stream)
+        self._apply(self._red, allgather_bufs, slot_offsets, stream)
+
+    def micro_step(self, grad_bufs, elem_offsets, op=ZERO_AVG, first=False, last=False,
+                   stream=None):
+        """One micro-step of gradient accumulation for every unit, as
+        ShardOptimizer.micro_step: the first overwrites each unit's fp32
+        gradient shard, later ones add to it, and the last one takes every
+        unit's statistics into the shared state."""
+        self._check(grad_bufs, elem_offsets)
+        st = self.state if last else None
+        for u, (bufs, off) in enumerate(zip(grad_bufs, elem_offsets)):
+            fn = zero_grad_reduce_shard if first else zero_grad_accumulate_shard
+            fn(bufs, off, self.master[u].numel(), op, self._reduced(u), st, stream=stream)
+
+    def step_from_accumulated(self, allgather_bufs, slot_offsets, stream=None):
+        """The step of every unit on the shards accumulated by micro_step."""
+        self._check(allgather_bufs, slot_offsets)
+        if any(r is None for r in self._red):
+            raise RuntimeError("no accumulated gradient: call micro_step first")
+        self._apply(self._red, allgather_bufs, slot_offsets, stream)
 
     def step_from_reduced(self, grad_shards, allgather_bufs, slot_offsets, stream=None):
         """Statistics over every unit's reduced (fp32/fp16/bf16) shard, then the

@@ -96,3 +96,45 @@ def test_unit_lists_must_match(zf):
                                  HP)
     with pytest.raises(ValueError):
         opt.step_from_reduced([torch.zeros(8, device="cuda")], [None], [0])
+
+
+def test_units_accumulate_micro_steps(zf):
+    """Two units, two optimizer steps of three micro-steps each (the first
+    reduces, the others add into each unit's fp32 gradient shard, the last
+    takes the statistics of both); against the oracle's reduce and
+    accumulate per unit and one shard step over the concatenation."""
+    N, rank = 8, 5
+    units = [100_003, 40_000]
+    S = [zf.zero_flat_layout([t], N)["shard"] for t in units]
+    masters0 = [synth.normal_f32(synth.stream_key("mu-acc-master", u), rank * s, s, 0.02)
+                for u, s in enumerate(S)]
+    opt = zf.MultiShardOptimizer([to_dev(m0, 0) for m0 in masters0], HP, loss_scale=1024.0)
+    ref = OracleRank(np.concatenate(masters0), 1024.0, False)
+    ags = [torch.zeros(N * s, dtype=torch.bfloat16, device="cuda") for s in S]
+    cuts = np.cumsum(S)[:-1]
+    with pytest.raises(RuntimeError):
+        opt.step_from_accumulated(ags, [rank * s for s in S])
+    for step in range(2):
+        accs = [np.zeros(s, np.float32) for s in S]
+        for micro in range(3):
+            bufs = [[synth.normal(synth.stream_key("mu-acc-grad", u, step, micro, k), 0, N * s,
+                                  1e-3, orc.BF16) for k in range(N)] for u, s in enumerate(S)]
+            opt.micro_step([[to_dev(b, orc.BF16) for b in bu] for bu in bufs],
+                           [rank * s for s in S], first=micro == 0, last=micro == 2)
+            for u, s in enumerate(S):
+                if micro == 0:
+                    accs[u] = orc.reduce(bufs[u], orc.BF16, rank * s, s, orc.AVG)
+                else:
+                    orc.reduce_accumulate(bufs[u], orc.BF16, rank * s, s, orc.AVG, accs[u])
+        for u in range(len(S)):
+            assert_bitwise(to_host(opt._red[u]), accs[u], "unit %d accumulated step %d" % (u, step))
+        opt.step_from_accumulated(ags, [rank * s for s in S])
+        res = ref.step(np.concatenate(accs), orc.F32, HP, orc.BF16)
+        st = opt.state.read()
+        assert st.last_skipped == 0 and st.step == step + 1
+        assert abs(st.last_norm - res["norm"]) <= sum(S) * 2.0 ** -53 * res["norm"]
+        assert st.last_coef == res["coef"]
+        for u, (p, lp) in enumerate(zip(np.split(ref.p, cuts), np.split(res["lp"], cuts))):
+            assert_bitwise(to_host(opt.master[u]), p, "unit %d master step %d" % (u, step))
+            assert_bitwise(to_host(ags[u][rank * S[u]:(rank + 1) * S[u]]), lp,
+                           "unit %d slot step %d" % (u, step))
