@@ -174,14 +174,15 @@ class MultiShardOptimizer:
         return self._red[u]
 
     def step_from_rank_buffers(self, grad_bufs, elem_offsets, allgather_bufs, slot_offsets,
-                               op=ZERO_AVG, stream=None):
+                               op=ZERO_AVG, quant=None, stream=None):
         """grad_bufs[u]: unit u's N rank gradient buffers; the reduce of each
-        unit with its statistics, then the step of every unit."""
+        unit with its statistics, then the step of every unit (with the INT8
+        payloads of `quant`, see _apply)."""
         self._check(grad_bufs, elem_offsets, allgather_bufs, slot_offsets)
         for u, (bufs, off) in enumerate(zip(grad_bufs, elem_offsets)):
             zero_grad_reduce_shard(bufs, off, self.master[u].numel(), op, self._reduced(u),
                                    self.state, stream=stream)
-        self._apply(self._red, allgather_bufs, slot_offsets, stream)
+        self._apply(self._red, allgather_bufs, slot_offsets, stream, quant)
 
     def micro_step(self, grad_bufs, elem_offsets, op=ZERO_AVG, first=False, last=False,
                    stream=None):
@@ -195,24 +196,31 @@ class MultiShardOptimizer:
             fn = zero_grad_reduce_shard if first else zero_grad_accumulate_shard
             fn(bufs, off, self.master[u].numel(), op, self._reduced(u), st, stream=stream)
 
-    def step_from_accumulated(self, allgather_bufs, slot_offsets, stream=None):
+    def step_from_accumulated(self, allgather_bufs, slot_offsets, quant=None, stream=None):
         """The step of every unit on the shards accumulated by micro_step."""
         self._check(allgather_bufs, slot_offsets)
         if any(r is None for r in self._red):
             raise RuntimeError("no accumulated gradient: call micro_step first")
-        self._apply(self._red, allgather_bufs, slot_offsets, stream)
+        self._apply(self._red, allgather_bufs, slot_offsets, stream, quant)
 
-    def step_from_reduced(self, grad_shards, allgather_bufs, slot_offsets, stream=None):
+    def step_from_reduced(self, grad_shards, allgather_bufs, slot_offsets, quant=None,
+                          stream=None):
         """Statistics over every unit's reduced (fp32/fp16/bf16) shard, then the
         step of every unit."""
         self._check(grad_shards, allgather_bufs, slot_offsets)
         for u, g in enumerate(grad_shards):
             zero_unscale_norm(g, self.state, n=self.master[u].numel(), stream=stream)
-        self._apply(grad_shards, allgather_bufs, slot_offsets, stream)
+        self._apply(grad_shards, allgather_bufs, slot_offsets, stream, quant)
 
-    def _apply(self, grads, allgather_bufs, slot_offsets, stream):
+    def _apply(self, grads, allgather_bufs, slot_offsets, stream, quant=None):
+        """quant: None, or per unit None or (q_buf, q_scales, q_slot_offset,
+        q_scale_offset) for that unit's blockwise-INT8 All-Gather payload."""
+        if quant is not None:
+            self._check(quant)
         last = len(grads) - 1
         for u, g in enumerate(grads):
+            q = quant[u] if quant is not None and quant[u] is not None else (None, None, 0, 0)
             zero_adamw_shard_step(g, self.master[u], self.exp_avg[u], self.exp_avg_sq[u],
                                   allgather_bufs[u], slot_offsets[u], self.hp, self.state,
-                                  finalize=u == last, stream=stream)
+                                  q_buf=q[0], q_scales=q[1], q_slot_offset=q[2],
+                                  q_scale_offset=q[3], finalize=u == last, stream=stream)

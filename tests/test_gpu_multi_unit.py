@@ -138,3 +138,41 @@ def test_units_accumulate_micro_steps(zf):
             assert_bitwise(to_host(opt.master[u]), p, "unit %d master step %d" % (u, step))
             assert_bitwise(to_host(ags[u][rank * S[u]:(rank + 1) * S[u]]), lp,
                            "unit %d slot step %d" % (u, step))
+
+
+def test_units_int8_payloads(zf):
+    """Pre-reduced bf16 gradients of three units, two steps, the first two
+    units also emitting their blockwise-INT8 All-Gather payload (blocks of 256
+    restarting at each unit's slot), the third none: codes and scales equal
+    the oracle's quantisation of each unit's written slot."""
+    N, rank = 64, 63
+    units = [1_000_003, 77_777, 4_096]
+    S = [zf.zero_flat_layout([t], N)["shard"] for t in units]
+    nb = [-(-s // 256) for s in S]
+    masters0 = [synth.normal_f32(synth.stream_key("mu-q-master", u), rank * s, s, 0.02)
+                for u, s in enumerate(S)]
+    opt = zf.MultiShardOptimizer([to_dev(m0, 0) for m0 in masters0], HP, loss_scale=1.0)
+    ref = OracleRank(np.concatenate(masters0), 1.0, False)
+    ags = [torch.zeros(N * s, dtype=torch.bfloat16, device="cuda") for s in S]
+    qs = [torch.zeros(N * s, dtype=torch.int8, device="cuda") for s in S[:2]]
+    scs = [torch.zeros(N * b, device="cuda") for b in nb[:2]]
+    quant = [(qs[0], scs[0], rank * S[0], rank * nb[0]), (qs[1], scs[1], rank * S[1], rank * nb[1]),
+             None]
+    cuts = np.cumsum(S)[:-1]
+    for step in range(2):
+        gs = [synth.normal(synth.stream_key("mu-q-grad", u, step), rank * s, s, 1e-3, orc.BF16)
+              for u, s in enumerate(S)]
+        opt.step_from_reduced([to_dev(g, orc.BF16) for g in gs], ags, [rank * s for s in S],
+                              quant=quant)
+        res = ref.step(np.concatenate([orc.bf16_to_f32(g) for g in gs]), orc.F32, HP, orc.BF16)
+        st = opt.state.read()
+        assert st.last_coef == res["coef"] and st.last_skipped == 0
+        for u, lp in enumerate(np.split(res["lp"], cuts)):
+            got = to_host(ags[u][rank * S[u]:(rank + 1) * S[u]])
+            assert_bitwise(got, lp, "unit %d slot step %d" % (u, step))
+            if u < 2:
+                rq, rs = orc.quant_int8(lp, orc.BF16, 256)
+                assert_bitwise(to_host(qs[u][rank * S[u]:]).view(np.uint8), rq.view(np.uint8),
+                               "unit %d codes step %d" % (u, step))
+                assert_bitwise(to_host(scs[u][rank * nb[u]:]), rs, "unit %d scales step %d" % (u, step))
+                assert not qs[u][:rank * S[u]].any() and not scs[u][:rank * nb[u]].any()
