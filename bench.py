@@ -10,7 +10,11 @@ GPU before timing) and resident in HBM when the timed region starts.
 
 A "step" is the whole path: statistics kernel + fold, the AdamW kernel, and
 the loss-scaler finalize.  The AdamW kernel is the dominant one; its duration
-is taken with HIP events on the launch stream around every launch.
+is taken with HIP events on the launch stream around every launch.  The same
+process measures the practical ceilings: read-only, write-only and copy streams
+over 4 GiB, and on the step's own arrays (whose physical placement moves every
+streaming kernel on them) the update's byte mix and a plain copy; `roofline`
+gives the AdamW rate against 8 TB/s and against each of these.
 
 Also timed, each as whole steps: the other workloads (8- and 64-way reduces,
 the 70B INT8 shard, the 7B block, the Tiny MLP, gradient accumulation over 2
