@@ -23,7 +23,8 @@ ZERO_MAX_PARTIALS = 65536
 EXPORTS = ("zero_last_error", "zero_flat_layout", "zero_step_state_init",
            "zero_grad_reduce_shard", "zero_unscale_norm", "zero_adamw_shard_step",
            "zero_quant_allgather_slot", "zero_dequant_allgather", "zero_grad_accumulate_shard",
-           "zero_grad_reduce_shard_int8", "zero_offload_adamw_host", "zero_offload_step")
+           "zero_grad_reduce_shard_int8", "zero_offload_adamw_host", "zero_offload_step",
+           "zero_grad_reduce_shard_noalloc")
 
 
 class zero_span_t(C.Structure):
@@ -72,6 +73,8 @@ def _load():
     L.zero_step_state_init.argtypes = [vp, C.c_float, i32, i32, C.c_float]
     L.zero_grad_reduce_shard.restype = C.c_int
     L.zero_grad_reduce_shard.argtypes = [vp, i32, i32, i64, i64, i32, vp, vp, vp]
+    L.zero_grad_reduce_shard_noalloc.restype = C.c_int
+    L.zero_grad_reduce_shard_noalloc.argtypes = [vp, i32, i32, i64, i64, i32, vp, vp, vp]
     L.zero_unscale_norm.restype = C.c_int
     L.zero_unscale_norm.argtypes = [vp, i32, i64, vp, vp]
     L.zero_adamw_shard_step.restype = C.c_int
@@ -175,6 +178,7 @@ def zero_flat_layout(numels, n_ranks, align=1, param_bytes=2, grad_bytes=2, opti
 
 # ------------------------------------------------------------------ state
 STATE_BYTES = C.sizeof(zero_step_state_t)
+STATE_HEADER_BYTES = zero_step_state_t.partials.offset   # all zero_grad_reduce_shard_noalloc uses
 
 
 def zero_step_state_init(loss_scale, dynamic, window=1000, min_scale=1.0):
@@ -213,14 +217,14 @@ class StepState:
         return C.c_void_p(self.buf.data_ptr())
 
 
-def _state_ptr(state):
+def _state_ptr(state, need=STATE_BYTES):
     if state is None:
         return None
     if isinstance(state, StepState):
         return state.ptr()
     _dev(state, "state", ("uint8",))
-    if state.numel() < STATE_BYTES:
-        raise ValueError("state must hold %d bytes" % STATE_BYTES)
+    if state.numel() < need:
+        raise ValueError("state must hold %d bytes" % need)
     return C.c_void_p(state.data_ptr())
 
 
@@ -248,6 +252,19 @@ def zero_grad_reduce_shard(grad_bufs, elem_offset, shard_numel, op, red_out, sta
     dt, arr = _rank_buffers(grad_bufs, elem_offset, shard_numel, red_out)
     _check(_lib.zero_grad_reduce_shard(arr, len(grad_bufs), dt, elem_offset, shard_numel, op,
                                        _ptr(red_out), _state_ptr(state), _stream(stream)))
+
+
+def zero_grad_reduce_shard_noalloc(grad_bufs, elem_offset, shard_numel, op, red_out, state=None,
+                                   stream=None):
+    """zero_grad_reduce_shard for callers that cannot allocate: the statistics'
+    partial sums live in the library's per-device scratch, so `state` may be a
+    uint8 device tensor of only STATE_HEADER_BYTES bytes.  Calls that overlap
+    in time on one device race on that scratch."""
+    dt, arr = _rank_buffers(grad_bufs, elem_offset, shard_numel, red_out)
+    _check(_lib.zero_grad_reduce_shard_noalloc(arr, len(grad_bufs), dt, elem_offset, shard_numel,
+                                               op, _ptr(red_out),
+                                               _state_ptr(state, STATE_HEADER_BYTES),
+                                               _stream(stream)))
 
 
 def zero_grad_accumulate_shard(grad_bufs, elem_offset, shard_numel, op, acc, state=None,

@@ -4,6 +4,7 @@
 // Nothing here allocates device memory or synchronizes.
 #include <math.h>
 #include <stdarg.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -40,6 +41,14 @@ int hip_fail(int e, const char* where) {
 bool valid_dtype(int32_t d) { return d == ZERO_F32 || d == ZERO_F16 || d == ZERO_BF16; }
 int esize(int32_t d) { return d == ZERO_F32 ? 4 : 2; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// the device address of the state's per-block partial-sum table (the state
+// pointer is a device address: computed, never dereferenced, here)
+double* state_partials(zero_step_state_t* st) {
+    return st ? reinterpret_cast<double*>(reinterpret_cast<char*>(st) +
+                                          offsetof(zero_step_state_t, partials))
+              : nullptr;
+}
 
 // a*b, false on int64 overflow
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
@@ -150,11 +159,13 @@ int zero_step_state_init(zero_step_state_t* st, float loss_scale, int32_t dynami
 
 // ---------------------------------------------------------------------------
 namespace {
-// zero_grad_reduce_shard and zero_grad_accumulate_shard: the same reduce, the
-// second adding into its output instead of overwriting it.
+// zero_grad_reduce_shard, zero_grad_accumulate_shard and
+// zero_grad_reduce_shard_noalloc: the same reduce, the second adding into its
+// output instead of overwriting it, the third keeping the statistics' partial
+// sums in the library's device scratch instead of the state.
 int reduce_entry(const char* fn, const void* const* grad_bufs, int32_t n_ranks, int32_t in_dtype,
                  int64_t elem_offset, int64_t shard_numel, int32_t op, float* red_out,
-                 int accumulate, zero_step_state_t* d_state, void* stream) {
+                 int accumulate, zero_step_state_t* d_state, void* stream, bool noalloc = false) {
     if (!grad_bufs) return fail(ZERO_EINVAL, "%s: grad_bufs is NULL", fn);
     if (n_ranks < 1 || n_ranks > ZERO_MAX_RANKS)
         return fail(ZERO_ERANGE, "%s: n_ranks %d not in [1, %d]", fn, n_ranks, ZERO_MAX_RANKS);
@@ -188,7 +199,8 @@ int reduce_entry(const char* fn, const void* const* grad_bufs, int32_t n_ranks, 
     a.red_out = red_out;
     a.accumulate = accumulate;
     a.st = d_state;
-    const int e = zf::launch_reduce_stats(a, stream);
+    a.partials = state_partials(d_state);
+    const int e = noalloc ? zf::launch_reduce_noalloc(a, stream) : zf::launch_reduce_stats(a, stream);
     if (e) return hip_fail(e, fn);
     return ok();
 }
@@ -199,6 +211,17 @@ int zero_grad_reduce_shard(const void* const* grad_bufs, int32_t n_ranks, int32_
                            float* red_out, zero_step_state_t* d_state, void* stream) {
     return reduce_entry("zero_grad_reduce_shard", grad_bufs, n_ranks, in_dtype, elem_offset,
                         shard_numel, op, red_out, 0, d_state, stream);
+}
+
+// The same reduce for callers that cannot allocate: the statistics' partial
+// sums go to the library's per-device scratch, so d_state needs only the
+// header of zero_step_state_t.
+int zero_grad_reduce_shard_noalloc(const void* const* grad_bufs, int32_t n_ranks,
+                                   int32_t in_dtype, int64_t elem_offset, int64_t shard_numel,
+                                   int32_t op, float* red_out, zero_step_state_t* d_state,
+                                   void* stream) {
+    return reduce_entry("zero_grad_reduce_shard_noalloc", grad_bufs, n_ranks, in_dtype,
+                        elem_offset, shard_numel, op, red_out, 0, d_state, stream, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -230,6 +253,7 @@ int zero_unscale_norm(const void* grad_shard, int32_t dtype, int64_t n, zero_ste
     a.n = n;
     a.red_out = nullptr;
     a.st = d_state;
+    a.partials = state_partials(d_state);
     const int e = zf::launch_reduce_stats(a, stream);
     if (e) return hip_fail(e, "zero_unscale_norm");
     return ok();
@@ -363,6 +387,7 @@ int zero_grad_reduce_shard_int8(const int8_t* const* q_bufs, const float* const*
     a.block = block;
     a.block_shift = (block & (block - 1)) == 0 ? __builtin_ctz((unsigned)block) : -1;
     a.st = d_state;
+    a.partials = state_partials(d_state);
     const int e = zf::launch_reduce_q8(a, stream);
     if (e) return hip_fail(e, fn);
     return ok();

@@ -30,6 +30,9 @@
 // dispatcher balances blocks as they retire.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "zf_launch.h"
@@ -262,9 +265,10 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // ---------------------------------------------------------------- reduce + statistics
 // red[i] = sum over buffers in rank order (fp32), AVG -> / n_ranks; optional
 // statistics of u = red * (1/loss_scale): per-block fp64 partial of u^2 into
-// st->partials[block] and an overflow flag.  A fold kernel adds the partials
-// into st->sumsq in a fixed order, so the sum is reproducible.  The partials
-// bound the grid (at most ZERO_MAX_PARTIALS blocks).
+// partials[block] (the state's table, or the library's device scratch) and an
+// overflow flag.  A fold kernel adds the partials into st->sumsq in a fixed
+// order, so the sum is reproducible.  The partials bound the grid (at most
+// ZERO_MAX_PARTIALS blocks).
 //
 // Mapping (quad, as the AdamW kernel): in chunk j of a tile, lane l owns
 // elements 256j + 4l .. 4l+3, so every wave instruction covers one contiguous
@@ -568,21 +572,24 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
         const int ovf = !isfinite(mine);
         const double bs = block_sum(mine);
         if (threadIdx.x == 0) {
-            a.st->partials[blockIdx.x] = bs;
+            a.partials[blockIdx.x] = bs;
             if (blockIdx.x == 0) a.st->n_partials = (int32_t)gridDim.x;
         }
         if (__ballot(ovf) != 0ull && lane == 0) atomicOr(&a.st->overflow, 1);
     }
 }
 
-// st->sumsq += partials[0..n_partials), fixed order (one block)
+// st->sumsq += partials[0..n_partials), fixed order (one block); partials is
+// the state's own table, or the library's device scratch (the no-allocation
+// reduce entry point)
 // One block of kFoldThreads: thread t adds partials t, t + kFoldThreads, ...
 // in that order, with kFoldU loads in flight (an out-of-range slot adds +0,
 // which leaves a sum of non-negative terms unchanged); then the waves'
 // butterflies and the waves in index order.
 constexpr int kFoldThreads = 1024;
 constexpr int kFoldU = 8;
-__global__ void __launch_bounds__(kFoldThreads) fold_kernel(zero_step_state_t* st) {
+__global__ void __launch_bounds__(kFoldThreads) fold_kernel(zero_step_state_t* st,
+                                                            const double* partials) {
     const int n = st->n_partials;
     double s = 0.0;
     for (int i0 = threadIdx.x; i0 < n; i0 += kFoldThreads * kFoldU) {
@@ -590,7 +597,7 @@ __global__ void __launch_bounds__(kFoldThreads) fold_kernel(zero_step_state_t* s
 #pragma unroll
         for (int u = 0; u < kFoldU; ++u) {
             const int i = i0 + u * kFoldThreads;
-            v[u] = i < n ? st->partials[i] : 0.0;
+            v[u] = i < n ? partials[i] : 0.0;
         }
 #pragma unroll
         for (int u = 0; u < kFoldU; ++u) s += v[u];
@@ -1099,7 +1106,8 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (STATS) {
-        hipLaunchKernelGGL(fold_kernel, dim3(1), dim3(kFoldThreads), 0, (hipStream_t)stream, a.st);
+        hipLaunchKernelGGL(fold_kernel, dim3(1), dim3(kFoldThreads), 0, (hipStream_t)stream, a.st,
+                           a.partials);
         e = hipGetLastError();
     }
     return (int)e;
@@ -1166,6 +1174,60 @@ int launch_reduce_stats(const ReduceLaunch& a, void* stream) {
         case ZERO_F16: return launch_reduce_v<ZERO_F16>(a, stream);
         default: return launch_reduce_v<ZERO_BF16>(a, stream);
     }
+}
+
+}  // namespace zf
+
+// ---------------------------------------------------------------- library-owned scratch
+// The statistics' per-block partial sums for zero_grad_reduce_shard_noalloc,
+// for callers that cannot allocate: one array per device, held until the
+// process ends.  Every such call on a device shares it (calls that overlap on
+// one device race); each launch writes every partial it later folds, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) double scratch[ZERO_MAX_PARTIALS];
+
+namespace zf {
+namespace {
+// scratch's device address on each device, looked up once per device (with
+// that device current) on the first no-allocation call there.  In host code
+// the array's name is only a stand-in for the symbol; kernels get this
+// address instead.
+constexpr int kMaxDevices = 64;
+std::atomic<double*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_for_current_device(double** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    double* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void* addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return (int)e;
+            if (!addr) return (int)hipErrorInvalidSymbol;
+            p = static_cast<double*>(addr);
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return 0;
+}
+}  // namespace
+
+int launch_reduce_noalloc(ReduceLaunch& a, void* stream) {
+    if (a.st) {
+        // the grid never exceeds ZERO_MAX_PARTIALS blocks (runs lengthen
+        // instead), which is what the scratch holds
+        static_assert(kMaxGridReduce <= ZERO_MAX_PARTIALS, "scratch smaller than the grid cap");
+        int e = scratch_for_current_device(&a.partials);
+        if (e) return e;
+    }
+    return launch_reduce_stats(a, stream);
 }
 
 int launch_adamw(const AdamLaunch& a, void* stream) {

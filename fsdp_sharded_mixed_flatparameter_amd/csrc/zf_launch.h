@@ -23,8 +23,14 @@ struct ReduceLaunch {
     int32_t block;          // INT8 payload only: elements per scale
     int32_t block_shift;    // log2(block) if a power of two, else -1
     zero_step_state_t* st;  // may be null
+    double* partials;       // per-block partial sums of the statistics (st set):
+                            // st->partials, or the library's scratch
 };
 int launch_reduce_stats(const ReduceLaunch& a, void* stream);
+// The same launch with the statistics' partial sums in the library's own
+// device scratch (one array per device, found on the first call on a device)
+// instead of the state's table; the state then needs only its header.
+int launch_reduce_noalloc(ReduceLaunch& a, void* stream);
 // The quantised-gradient reduce: bufs[2k] = rank k's INT8 codes, bufs[2k+1]
 // its fp32 block scales (n_ranks <= ZERO_MAX_RANKS / 2).
 int launch_reduce_q8(const ReduceLaunch& a, void* stream);

@@ -45,7 +45,8 @@
  *     failure zero_last_error() returns a thread-local message.  Arguments are
  *     validated before anything is launched: on error nothing ran.
  *   - Device pointers are owned by the caller; the library never allocates
- *     or frees device memory.  Except for the ZeRO-Offload step (section 8),
+ *     or frees device memory (its one static array, the scratch of
+ *     zero_grad_reduce_shard_noalloc, is placed with the code).  Except for the ZeRO-Offload step (section 8),
  *     which runs on host threads and returns when done, no call allocates
  *     host memory or synchronizes.  The library cannot see allocation sizes:
  *     the caller vouches that every range it names is allocated.
@@ -61,6 +62,7 @@
 #ifndef ZEROFLAT_H
 #define ZEROFLAT_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -196,6 +198,29 @@ int zero_step_state_init(zero_step_state_t* host_state, float loss_scale, int32_
 int zero_grad_reduce_shard(const void* const* grad_bufs, int32_t n_ranks, int32_t in_dtype,
                            int64_t elem_offset, int64_t shard_numel, int32_t op,
                            float* red_out, zero_step_state_t* d_state, void* stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): zero_grad_reduce_shard
+ * with the same arguments, results and errors, except that the statistics'
+ * per-block partial sums live in the library's own device memory -- one
+ * static array of ZERO_MAX_PARTIALS doubles (512 KiB) per device, held until
+ * the process ends -- instead of d_state->partials.  d_state (when not NULL)
+ * then needs only its first ZERO_STEP_STATE_HEADER_BYTES bytes; the library
+ * neither reads nor writes the partials table of the caller's state.  A
+ * launch never needs more partial sums than the array holds, at any shard
+ * size (each wave's run of tiles lengthens instead), so no size is refused on
+ * its account; the other limits are zero_grad_reduce_shard's.  The call
+ * allocates nothing, host or device: the array's device address is looked up
+ * once per device, on the first call made with that device current.  Every
+ * such call on one device shares the array, so calls that overlap in time on
+ * one device (two streams, or two host threads) race and must be ordered by
+ * the caller; each launch writes every partial sum it folds, so nothing
+ * carries over from one call to the next. */
+#define ZERO_STEP_STATE_HEADER_BYTES ((int64_t)offsetof(zero_step_state_t, partials))
+int zero_grad_reduce_shard_noalloc(const void* const* grad_bufs, int32_t n_ranks,
+                                   int32_t in_dtype, int64_t elem_offset, int64_t shard_numel,
+                                   int32_t op, float* red_out, zero_step_state_t* d_state,
+                                   void* stream);
 
 /* Statistics only, over an already reduced fp32 shard or a pre-reduced
  * fp16/bf16 gradient shard (DEVICE grad_shard[n] of `dtype`): the sumsq /
