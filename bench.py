@@ -10,18 +10,25 @@ GPU before timing) and resident in HBM when the timed region starts.
 
 A "step" is the whole path: statistics kernel + fold, the AdamW kernel, and
 the loss-scaler finalize.  The AdamW kernel is the dominant one; its duration
-is taken with HIP events on the launch stream around every launch.  The same
-process measures the practical ceilings: read-only, write-only and copy streams
-over 4 GiB, and on the step's own arrays (whose physical placement moves every
-streaming kernel on them) the update's byte mix and a plain copy; `roofline`
-gives the AdamW rate against 8 TB/s and against each of these.
+is taken with HIP events on the launch stream around every launch.  Where the
+step's arrays land in physical memory moves every streaming kernel on them,
+so the arrays are allocated afresh three times, each allocation running the
+warm-up and the timed steps; `value` and `roofline` cover all of them and
+`allocations` lists each with the median and minimum.  The same process
+measures the practical ceilings: read-only, write-only and copy streams over
+4 GiB, and on the step's own arrays the update's byte mix and a plain copy;
+`roofline` gives the AdamW rate against 8 TB/s, against each of these, and
+against the read-only and write-only rates taken back to back for its 14 B
+read and 14 B written per parameter.
 
 Also timed, each as whole steps: the other workloads (8- and 64-way reduces,
 the 70B INT8 shard, the 7B block, the Tiny MLP, gradient accumulation over 2
 micro-steps, INT8-quantised rank gradients), the ZeRO-Offload step (the
 update on host cores), and the INT8 All-Gather consumer (gathered slots
 dequantised into the full flat parameter) on the 7B block and the whole 70B
-flat parameter.
+flat parameter.  The oracle is timed on one host core beside the headline and
+beside every other workload (the full shard for the Tiny MLP, the 1.5B/64
+shard and the 7B block; a window of the shard for the others).
 
 Prints ONE JSON line.  --gpus N with N > 1 exits: the library runs one rank's
 step on one GPU.
@@ -44,6 +51,7 @@ ADAM_BYTES_PER_PARAM = {        # algorithmic bytes of one AdamW-kernel launch p
 KERNEL_SOURCE = os.path.join(ROOT, "fsdp_sharded_mixed_flatparameter_amd", "csrc",
                              "zeroflat_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_10b_n8_hbm_traffic.txt")
+N_ALLOC = 3                     # fresh allocations of the headline step's arrays
 VARIANTS = (   # the other workloads, whole steps each (parity cases in tests/ as well)
     ("10b_n8_reduce8", "10B/8 rank-7 shard with the 8 raw fp16 rank slices reduced (AVG) in the step"),
     ("70b_n64_int8", "70B/64 rank-63 shard (1.09e9), pre-reduced bf16, clipping active, bf16 "
@@ -137,6 +145,99 @@ def cpu_baseline(w, window=1 << 26, steps=5):
                       "the oracle's statistics + AdamW + fp16 write-back, one thread pinned to "
                       "core %d; %.1f s" % (window, start, steps, core, dt),
             "host": {"cpu_model": cpu_model(), "cores_available": len(allowed)}}
+
+
+# The oracle on every other workload: the full shard where the oracle finishes
+# in seconds (the Tiny MLP, the 1.5B/64 shard, the 7B block), else a window of
+# the same shard; (window or None, steps).
+CPU_SAMPLES = {
+    "tiny_mlp_n4": (None, 10),
+    "gpt1p5b_n64": (None, 1),
+    "llama7b_block_n8": (None, 2),
+    "10b_n8_reduce8": (1 << 24, 2),
+    "70b_n64_int8": (1 << 24, 3),
+    "10b_n8_accum2": (1 << 24, 1),
+    "10b_n8_qg": (1 << 24, 2),
+    "gpt1p5b_n64_qg": (1 << 22, 2),
+}
+
+
+def _host_normal(torch, key, start, n, sigma, dtype):
+    """Host array of the seeded generator's values (filled by the generator's
+    device implementation, which is bit-identical to its host one, then
+    copied down: input generation is not timed)."""
+    import numpy as np
+    from synth import synth
+    tdt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[dtype]
+    t = torch.empty(n, dtype=tdt, device="cuda")
+    synth.fill_normal(t, key, start, sigma)
+    if dtype == 0:
+        return t.cpu().numpy()
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_baseline_workload(torch, w, window, steps):
+    """The oracle as it stands on one workload's step (the same inputs as the
+    GPU variant: the step-0 gradients, reused every step), one thread pinned
+    to one core; inputs generated first, untimed."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    from synth.workloads import key_grad, key_grad_micro, key_grad_reduced, key_master
+    n = w.shard if window is None else min(window, w.shard)
+    start = w.start
+    p = _host_normal(torch, key_master(w), start, n, w.master_sigma, 0)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    sc = orc.make_scaler(w.loss_scale, w.dynamic, w.window)
+    hp = orc.Hparams(**w.hp)
+    gd = w.grad_dtype
+    if w.grad_int8:   # the senders' quantisation of their slices (not timed)
+        qs, ss = [], []
+        for k in range(w.n_ranks):
+            q, s_ = orc.quant_int8(_host_normal(torch, key_grad(w, 0, k), start, n, w.grad_sigma,
+                                                gd), gd, 256)
+            qs.append(q)
+            ss.append(s_)
+    elif w.micro_steps > 1:
+        micro = [[_host_normal(torch, key_grad_micro(w, 0, mi, k), start, n, w.grad_sigma, gd)
+                  for k in range(w.n_ranks)] for mi in range(w.micro_steps)]
+    elif w.reduce:
+        bufs = [_host_normal(torch, key_grad(w, 0, k), start, n, w.grad_sigma, gd)
+                for k in range(w.n_ranks)]
+    else:
+        g = _host_normal(torch, key_grad_reduced(w, 0), start, n, w.grad_sigma, gd)
+    torch.cuda.empty_cache()
+
+    def one():
+        if w.grad_int8:
+            grad, gdt = orc.reduce_q8(qs, ss, n, 256, w.op), orc.F32
+        elif w.micro_steps > 1:
+            grad, gdt = orc.reduce(micro[0], gd, 0, n, w.op), orc.F32
+            for mi in range(1, w.micro_steps):
+                orc.reduce_accumulate(micro[mi], gd, 0, n, w.op, grad)
+        elif w.reduce:
+            grad, gdt = orc.reduce(bufs, gd, 0, n, w.op), orc.F32
+        else:
+            grad, gdt = g, gd
+        orc.shard_step(grad=grad, grad_dtype=gdt, master=p, exp_avg=m, exp_avg_sq=v, scaler=sc,
+                       hp=hp, param_dtype=w.param_dtype, quant_block=w.quant_block or None)
+
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            one()
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, allowed)
+    what = "full %d-parameter shard" % n if window is None or n == w.shard else \
+        "%d-parameter window of the %d-parameter shard" % (n, w.shard)
+    return {"value": n * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": "%s, %d step(s) of the oracle's whole step, one thread pinned to core %d; "
+                      "%.1f s" % (what, steps, core, dt)}
 
 
 def cpu_model():
@@ -445,7 +546,11 @@ def run_offload(zf, torch, w, steps, warmup):
     from synth import synth
     from synth.workloads import key_grad_reduced, key_master
     S = w.shard
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    # the update's threads leave two of the cores this process may use to the
+    # HIP runtime's copy threads and this (Python) thread
+    cores = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0")) or cores
+    threads = max(1, min(cap, cores) - 2)
     master = torch.empty(S, dtype=torch.float32)
     tmp = torch.empty(S, dtype=torch.float32, device="cuda")
     synth.fill_normal(tmp, key_master(w), w.start, w.master_sigma)
@@ -506,6 +611,11 @@ def run_offload(zf, torch, w, steps, warmup):
             "host_GBps": host_bytes * S / wall / 1e9, "host_copy_ceiling_GBps": host_copy,
             "host_update_only_ms": host_only * 1e3,
             "host_update_only_GBps": host_bytes * S / host_only / 1e9,
+            # the link's copies read and write the same host memory: 2 B of
+            # gradient written and 2 B of parameters read per parameter on top
+            # of the update's 28 B, at the update's own host-memory rate
+            "host_memory_bound_ms": host_only * 1e3 * (host_bytes + 4) / host_bytes,
+            "frac_of_host_memory_bound": host_only * (host_bytes + 4) / host_bytes / wall,
             "what": "10B/8 rank-7 shard offloaded: fp32 state in host memory, AdamW on %d host "
                     "threads, fp16 gradient down and fp16 parameters up over the host link"
                     % threads}
@@ -565,14 +675,37 @@ def main():
     S = w.shard
 
     ceilings = run_ceilings(torch)
-    res = run_prereduced(zf, torch, w, args.steps, args.warmup)
-    ceilings["adamw_mix"] = res["mix"]
-    ceilings["copy_step_arrays"] = res["copy"]
-    ms_step = res["wall"] / args.steps * 1e3
-    adam_ms = sum(res["adam_ms"]) / len(res["adam_ms"])
+    # the headline over N_ALLOC fresh allocations of the step's arrays: where
+    # they land in physical memory moves every streaming kernel on them
+    allocs = [run_prereduced(zf, torch, w, args.steps, args.warmup) for _ in range(N_ALLOC)]
     adam_bytes = ADAM_BYTES_PER_PARAM["f16"] * S
-    achieved = adam_bytes / (adam_ms * 1e-3) / 1e9
     step_bytes = (2 + ADAM_BYTES_PER_PARAM["f16"]) * S           # + the statistics pass
+    each = []
+    for r in allocs:
+        ms = r["wall"] / args.steps * 1e3
+        am = sum(r["adam_ms"]) / len(r["adam_ms"])
+        each.append({"ms_per_step": ms, "params_per_s": S / (ms * 1e-3),
+                     "adam_avg_launch_ms": am, "adam_GBps": adam_bytes / (am * 1e-3) / 1e9,
+                     "adam_frac_of_peak": adam_bytes / (am * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                     "copy_step_arrays_GBps": r["copy"]["GBps"], "adamw_mix_GBps": r["mix"]["GBps"]})
+    all_adam = [x for r in allocs for x in r["adam_ms"]]
+    ms_step = sum(r["wall"] for r in allocs) / (N_ALLOC * args.steps) * 1e3
+    adam_ms = sum(all_adam) / len(all_adam)
+    achieved = adam_bytes / (adam_ms * 1e-3) / 1e9
+    mean = lambda xs: sum(xs) / len(xs)
+    ceilings["adamw_mix"] = dict(allocs[0]["mix"], GBps=mean([e["adamw_mix_GBps"] for e in each]),
+                                 what=allocs[0]["mix"]["what"] + "; mean over the allocations")
+    ceilings["copy_step_arrays"] = dict(allocs[0]["copy"],
+                                        GBps=mean([e["copy_step_arrays_GBps"] for e in each]),
+                                        what=allocs[0]["copy"]["what"] +
+                                        "; mean over the allocations")
+    # reads and writes share the HBM: the update's 14 B read and 14 B written
+    # per parameter at the read-only and write-only rates, back to back
+    rd = wr = 14 * S
+    t_add = rd / (ceilings["read"]["GBps"] * 1e9) + wr / (ceilings["write"]["GBps"] * 1e9)
+    additive = (rd + wr) / t_add / 1e9
+    pps = sorted(e["params_per_s"] for e in each)
+    agb = sorted(e["adam_GBps"] for e in each)
     out = {
         "metric": "sharded AdamW step: params updated/s and achieved HBM GB/s (% of peak) at 1 GPU",
         "value": S / (ms_step * 1e-3),
@@ -592,6 +725,12 @@ def main():
                                "write-back into the full All-Gather buffer at offset 8.75e9",
                    "shard_params": S, "n_ranks": w.n_ranks, "rank": w.rank,
                    "parallelism": "one rank's shard on 1 GPU"},
+        "allocations": {"n": N_ALLOC, "each": each,
+                        "params_per_s_median": pps[len(pps) // 2], "params_per_s_min": pps[0],
+                        "adam_GBps_median": agb[len(agb) // 2], "adam_GBps_min": agb[0],
+                        "what": "the step's arrays allocated afresh %d times, each running the "
+                                "warm-up and the %d timed steps; value, ms_per_step and roofline "
+                                "are over all of them" % (N_ALLOC, args.steps)},
         "step_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "roofline": {"bound": "hbm", "kernel": "adamw_kernel (fused AdamW + fp16 write-back)",
@@ -599,8 +738,10 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": read_traffic(),
                      "algorithmic_bytes_per_launch": adam_bytes,
                      "avg_launch_ms": adam_ms,
-                     "median_launch_ms": sorted(res["adam_ms"])[len(res["adam_ms"]) // 2],
-                     "min_launch_ms": min(res["adam_ms"]),
+                     "median_launch_ms": sorted(all_adam)[len(all_adam) // 2],
+                     "min_launch_ms": min(all_adam),
+                     "additive_read_write_GBps": additive,
+                     "frac_of_additive_read_write": achieved / additive,
                      "frac_of_copy_ceiling": achieved / ceilings["copy"]["GBps"],
                      "frac_of_mix_ceiling": achieved / ceilings["adamw_mix"]["GBps"],
                      "frac_of_step_array_copy": achieved / ceilings["copy_step_arrays"]["GBps"]},
@@ -612,6 +753,10 @@ def main():
             r = run_workload(zf, torch, WORKLOADS[name], max(3, args.steps // 2), 2,
                              flush=name in FLUSHED)
             r["what"] = what
+            if not args.no_cpu_baseline:
+                r["cpu_baseline"] = cpu_baseline_workload(torch, WORKLOADS[name],
+                                                          *CPU_SAMPLES[name])
+                r["cpu_baseline"]["gpu_over_oracle"] = r["params_per_s"] / r["cpu_baseline"]["value"]
             out["variants"][name] = r
         out["variants"]["tiny_mlp_n4_graph"] = run_graph(zf, torch, WORKLOADS["tiny_mlp_n4"],
                                                          max(20, args.steps), 5)
@@ -624,6 +769,7 @@ def main():
             out["allgather_consumer"][name] = r
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"]["gpu_over_oracle"] = out["value"] / out["cpu_baseline"]["value"]
     print(json.dumps(out), flush=True)
 
 
