@@ -7,9 +7,11 @@ generator; the oracle regenerates, on the host, exactly the elements it checks
   boundaries) are followed through every step by the oracle and compared bit
   for bit (master, m, v, the 16-bit slot, INT8 codes and scales of whole
   sampled blocks);
-- the global norm of a step is recomputed by the oracle over the whole shard
-  (chunks on host threads, each chunk summed by the oracle, chunk sums added in
-  order) and compared at 1e-5;
+- the global norm of every step of the 10B and 1.5B workloads is recomputed
+  by the oracle over the whole shard (chunks on host threads, each chunk
+  summed by the oracle, chunk sums added in order) and compared at 1e-5; from
+  step 1 on it reads host copies of the gradients the GPU read, whose sampled
+  values are checked against the host generator;
 - where the clip coefficient does not depend on the exact norm, that is shown
   by a bound that holds at any size (generator values are bounded by 6 sigma).
 """
@@ -77,6 +79,31 @@ def full_sumsq_prereduced(w, step, scale):
     return sum(p[0] for p in parts), int(any(p[1] for p in parts))
 
 
+def sumsq_of_host_shard(gh, dtype, scale):
+    """Oracle sum of squares over a host copy of a whole pre-reduced shard."""
+    def job(lo):
+        return orc.unscale_stats(np.ascontiguousarray(gh[lo:lo + CHUNK]), dtype, scale)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(job, range(0, gh.size, CHUNK)))
+    return sum(p[0] for p in parts), int(any(p[1] for p in parts))
+
+
+def sumsq_of_host_slices(slices, dtype, op, scale, chunk=1 << 21):
+    """Oracle reduce of host copies of the N rank slices, then the sum of
+    squares of the unscaled result, over the whole shard."""
+    S = slices[0].size
+
+    def job(lo):
+        n = min(chunk, S - lo)
+        red = orc.reduce([np.ascontiguousarray(b[lo:lo + n]) for b in slices], dtype, 0, n, op)
+        return orc.unscale_stats(red, orc.F32, scale)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(job, range(0, S, chunk)))
+    return sum(p[0] for p in parts), int(any(p[1] for p in parts))
+
+
 def full_sumsq_reduce(w, step, scale, chunk=1 << 20):
     S, start, N = w.shard, w.start, w.n_ranks
 
@@ -130,13 +157,14 @@ def test_10b_n8_rank7_full_size(zf):
         opt.step_from_reduced(g, ag, start)
         st = opt.state.read()
         gs = synth.normal_at(key_grad_reduced(w, step), start + idx, w.grad_sigma, w.grad_dtype)
-        if step in (0, w.steps - 1):
-            sumsq, ovf = full_sumsq_prereduced(w, step, w.loss_scale)
-            assert ovf == 0 and abs(st.last_norm - math.sqrt(sumsq)) <= 1e-5 * math.sqrt(sumsq)
-        else:
-            # the norm enters the update only through coef, which the bound fixes at
-            # exactly 1: any sum below the bound stands for it
-            sumsq, ovf = 0.0, 0
+        # the norm at every step: the oracle's sum over the whole shard, from the
+        # host copy of the gradient the GPU read (its sampled values are the
+        # generator's: they equal gs below)
+        gh = to_host(g)
+        assert_bitwise(gh[idx], gs, "gradient copy step %d" % step)
+        sumsq, ovf = sumsq_of_host_shard(gh, w.grad_dtype, w.loss_scale)
+        assert ovf == 0 and abs(st.last_norm - math.sqrt(sumsq)) <= 1e-5 * math.sqrt(sumsq)
+        del gh
         res = ref.step(gs, w.grad_dtype, w.hp, w.param_dtype, sumsq_local=sumsq,
                        overflow_local=ovf)
         assert res["coef"] == 1.0 and st.last_coef == 1.0 and st.last_skipped == 0
@@ -279,12 +307,18 @@ def test_gpt1p5b_n64_rank0_full_size(zf):
             synth.fill_normal(slices[k], key_grad(w, step, k), start, w.grad_sigma)
         opt.step_from_rank_buffers(slices, 0, ag, start)
         st = opt.state.read()
+        hb = [rank_grad_at(w, step, k, start + idx) for k in range(N)]
         if step == 0:
             sumsq, ovf = full_sumsq_reduce(w, step, w.loss_scale)
-            assert ovf == 0 and abs(st.last_norm - math.sqrt(sumsq)) <= 1e-5 * math.sqrt(sumsq)
         else:
-            sumsq, ovf = 0.0, 0   # enters only through coef, fixed at 1 by the bound
-        hb = [rank_grad_at(w, step, k, start + idx) for k in range(N)]
+            # the norm at every step: host copies of the slices the GPU read
+            # (their sampled values are the generator's: checked against hb)
+            host = [to_host(t) for t in slices]
+            for k in range(N):
+                assert_bitwise(host[k][idx], hb[k], "slice %d copy step %d" % (k, step))
+            sumsq, ovf = sumsq_of_host_slices(host, w.grad_dtype, w.op, w.loss_scale)
+            del host
+        assert ovf == 0 and abs(st.last_norm - math.sqrt(sumsq)) <= 1e-5 * math.sqrt(sumsq)
         red = orc.reduce(hb, w.grad_dtype, 0, idx.size, w.op)
         res = ref.step(red, orc.F32, w.hp, w.param_dtype, sumsq_local=sumsq, overflow_local=ovf)
         assert res["coef"] == 1.0 == st.last_coef and st.last_skipped == 0
