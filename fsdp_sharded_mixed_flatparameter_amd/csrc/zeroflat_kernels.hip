@@ -10,7 +10,9 @@
 //   finalize_kernel  loss scaler and counters
 //   quant_kernel     INT8 of an existing 16-bit slot (quad tiles)
 //   quant8_kernel    the same on 16-byte aligned slots, eight elements per lane
-//   dequant_kernel   the INT8 All-Gather consumer
+//   dequant_kernel   the INT8 All-Gather consumer, tiles per slot
+//   dequant_flat_kernel  the same with tiles over the flat output (slots of
+//                    2048 elements or more)
 //
 // Every kernel here streams HBM once: none is a contraction, so there is no
 // MFMA work; the design goals are wide coalesced accesses, enough bytes in
@@ -1048,6 +1050,66 @@ __global__ void __launch_bounds__(kThreads) dequant_kernel(DequantLaunch a, int 
     }
 }
 
+// The same consumer with tiles laid over the flat output instead of each slot:
+// every tile starts at a multiple of kDTile elements of the flat buffer, so a
+// tile's stores cover whole cache lines of the output (and its code loads
+// whole lines of the payload) whatever the slot size.  Tiled per slot, a slot
+// size that is not a multiple of the 128-byte line left every tile edge
+// splitting a line between two waves, and the counters showed those lines
+// written back in two parts (4-6% extra bytes on such sizes, none on aligned
+// ones).  Needs slot_numel >= kDTile (at most one slot boundary per tile) and
+// the quad path (slot_numel % 4 == 0: a lane quad never straddles a slot or a
+// block).
+template <int OT>
+__global__ void __launch_bounds__(kThreads) dequant_flat_kernel(DequantLaunch a, int block_shift) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_id = wave_index();
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int64_t S = a.slot_numel;
+    const int64_t total = S * a.n_slots;
+    const int64_t nb = (S + a.block - 1) / a.block;
+    const int64_t nfull = total / kDTile;
+    const int64_t ntiles = (total + kDTile - 1) / kDTile;
+    auto block_of = [&](int64_t i) -> int64_t {
+        return block_shift >= 0 ? (i >> block_shift) : i / a.block;
+    };
+    for (int64_t t = wave_id; t < ntiles; t += nwaves) {
+        const int64_t e0 = t * kDTile;
+        const int64_t s0 = e0 / S;          // slot of the tile's first element
+        const int64_t b1 = (s0 + 1) * S;    // first element of the next slot
+        // the scale of the block holding flat element i (slot s0 or s0 + 1)
+        auto scale_of = [&](int64_t i) -> float {
+            const int64_t sl = i >= b1 ? s0 + 1 : s0;
+            return a.qs[sl * nb + block_of(i - sl * S)];
+        };
+        if (t < nfull) {
+            uint32_t code[kDU];
+            float sc[kDU];
+#pragma unroll
+            for (int u = 0; u < kDU; ++u) {
+                const int64_t i = e0 + 256 * u + 4 * lane;
+                code[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.q + i));
+                sc[u] = scale_of(i);                 // 4 | S and 4 | block: one block per quad
+            }
+#pragma unroll
+            for (int u = 0; u < kDU; ++u) {
+                float x[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[c] = code_of(code[u], c) * sc[u];
+                store_out_quad<OT>(a.out, e0 + 256 * u + 4 * lane, x);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kDU; ++u)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t i = e0 + 256 * u + 4 * lane + c;
+                    if (i < total) store_out_one<OT>(a.out, i, (float)a.q[i] * scale_of(i));
+                }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launch helpers
 int grid_for_tiles(int64_t ntiles, int cap) {
     int64_t g = (ntiles + kWaves - 1) / kWaves;
@@ -1250,13 +1312,17 @@ int launch_adamw(const AdamLaunch& a, void* stream) {
 
 int launch_dequant(const DequantLaunch& a, void* stream) {
     const int64_t per_slot = (a.slot_numel + kDTile - 1) / kDTile;
-    const int grid = grid_for_tiles(per_slot * a.n_slots, kMaxGridStream);
+    const bool flat = a.vec && a.slot_numel >= kDTile;
+    const int64_t ntiles = flat ? (a.slot_numel * a.n_slots + kDTile - 1) / kDTile
+                                : per_slot * a.n_slots;
+    const int grid = grid_for_tiles(ntiles, kMaxGridStream);
     int shift = -1;
     if ((a.block & (a.block - 1)) == 0) shift = __builtin_ctz((unsigned)a.block);
     hipStream_t s = (hipStream_t)stream;
 #define ZF_DQ(OT)                                                                           \
     do {                                                                                    \
-        if (a.vec) hipLaunchKernelGGL((dequant_kernel<OT, true>), dim3(grid), dim3(kThreads), 0, s, a, shift); \
+        if (flat) hipLaunchKernelGGL((dequant_flat_kernel<OT>), dim3(grid), dim3(kThreads), 0, s, a, shift); \
+        else if (a.vec) hipLaunchKernelGGL((dequant_kernel<OT, true>), dim3(grid), dim3(kThreads), 0, s, a, shift); \
         else hipLaunchKernelGGL((dequant_kernel<OT, false>), dim3(grid), dim3(kThreads), 0, s, a, shift);      \
     } while (0)
     if (a.out_dtype == ZERO_F32) ZF_DQ(ZERO_F32);

@@ -48,6 +48,9 @@ DEQ_CASES = [
     (5, 4096 + 12, 64, 0, 0), (2, 3000, 12, 2, 0), (2, 2048, 256, 2, 1), (2, 4096, 4, 1, 0),
     (64, 20_000, 256, 2, 0), (7, 513, 256, 0, 0),
     (65536, 4, 4, 2, 0), (65536, 7, 256, 1, 0),    # the most slots per call (tiny slots)
+    # flat tiling (slot_numel >= 2048 and a multiple of 4): slot boundaries inside
+    # tiles, at offsets that are not multiples of a cache line
+    (3, 2052, 256, 2, 0), (5, 2196, 260, 1, 0), (3, 4100, 256, 0, 0), (2, 1_000_004, 256, 2, 0),
 ]
 
 
