@@ -344,12 +344,15 @@ def step_bytes_per_param(w):
 FLUSHED = ("tiny_mlp_n4", "llama7b_block_n8")   # working sets within a few times the 256 MB cache
 
 
-def run_workload(zf, torch, w, steps, warmup, flush=False):
+def run_workload(zf, torch, w, steps, warmup, flush=False, shift=0):
     """Whole steps of any workload (inputs generated on the GPU first).  With
     `flush`, a 512 MB scratch buffer is streamed before each timed step, so the
     step starts with none of its data in the 256 MB Infinity Cache, and each
     step is timed with HIP events around it; the back-to-back rate is kept
-    beside it."""
+    beside it.  With `shift` > 0 the rank slices (reduce workloads) start that
+    many elements into their buffers and the slot that many elements past its
+    place in the All-Gather buffer: the layout of a shard size that is not a
+    multiple of the vector width."""
     from synth import synth
     from synth.workloads import key_grad, key_grad_micro, key_grad_reduced, key_master
     S, dev = w.shard, torch.device("cuda:0")
@@ -382,19 +385,20 @@ def run_workload(zf, torch, w, steps, warmup, flush=False):
                 synth.fill_normal(b, key_grad_micro(w, 0, mi, k), w.start, w.grad_sigma)
                 grads[mi].append(b)
     elif w.reduce:
-        # rank-r slices of the N ranks' gradient buffers (slot-sized, offset 0)
+        # rank-r slices of the N ranks' gradient buffers (slot-sized, offset 0,
+        # or `shift` elements in)
         grads = []
         for k in range(w.n_ranks):
-            b = torch.empty(S, dtype=gdt, device=dev)
-            synth.fill_normal(b, key_grad(w, 0, k), w.start, w.grad_sigma)
+            b = torch.empty(S + shift, dtype=gdt, device=dev)
+            synth.fill_normal(b[shift:], key_grad(w, 0, k), w.start, w.grad_sigma)
             grads.append(b)
     else:
         grads = torch.empty(S, dtype=gdt, device=dev)
         synth.fill_normal(grads, key_grad_reduced(w, 0), w.start, w.grad_sigma)
     if w.full_allgather:
-        ag, off = torch.zeros(w.padded, dtype=pdt, device=dev), w.start
+        ag, off = torch.zeros(w.padded + shift, dtype=pdt, device=dev), w.start + shift
     else:
-        ag, off = torch.zeros(S, dtype=pdt, device=dev), 0
+        ag, off = torch.zeros(S + shift, dtype=pdt, device=dev), shift
     q = qs = None
     if w.quant_block:
         q = torch.zeros(S, dtype=torch.int8, device=dev)
@@ -409,7 +413,7 @@ def run_workload(zf, torch, w, steps, warmup, flush=False):
                 opt.micro_step(grads[mi], 0, op=w.op, first=mi == 0, last=mi == w.micro_steps - 1)
             opt.step_from_accumulated(ag, off, q_buf=q, q_scales=qs)
         elif w.reduce:
-            opt.step_from_rank_buffers(grads, 0, ag, off, op=w.op, q_buf=q, q_scales=qs)
+            opt.step_from_rank_buffers(grads, shift, ag, off, op=w.op, q_buf=q, q_scales=qs)
         else:
             opt.step_from_reduced(grads, ag, off, q_buf=q, q_scales=qs)
 
@@ -757,6 +761,15 @@ def main():
                 r["cpu_baseline"] = cpu_baseline_workload(torch, WORKLOADS[name],
                                                           *CPU_SAMPLES[name])
                 r["cpu_baseline"]["gpu_over_oracle"] = r["params_per_s"] / r["cpu_baseline"]["value"]
+            out["variants"][name] = r
+        # the same steps with every rank slice and the slot one element off
+        # the vector boundary (rank r's slice starts at r*S for any S)
+        for name, base in (("10b_n8_reduce8_shift1", "10b_n8_reduce8"),):
+            r = run_workload(zf, torch, WORKLOADS[base], max(3, args.steps // 2), 2, shift=1)
+            r["what"] = ("as %s, with every rank slice starting 1 element into its buffer and "
+                         "the slot 1 element past its place: the reduce's shifted vector path "
+                         "and an unaligned slot" % base)
+            r["vs_aligned"] = out["variants"][base]["ms_per_step"] / r["ms_per_step"]
             out["variants"][name] = r
         out["variants"]["tiny_mlp_n4_graph"] = run_graph(zf, torch, WORKLOADS["tiny_mlp_n4"],
                                                          max(20, args.steps), 5)

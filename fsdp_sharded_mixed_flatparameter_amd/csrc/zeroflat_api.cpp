@@ -42,6 +42,9 @@ bool valid_dtype(int32_t d) { return d == ZERO_F32 || d == ZERO_F16 || d == ZERO
 int esize(int32_t d) { return d == ZERO_F32 ? 4 : 2; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// the cache line the streaming reads are laid out on
+constexpr uintptr_t kLineBytes = 128;
+
 // the device address of the state's per-block partial-sum table (the state
 // pointer is a device address: computed, never dereferenced, here)
 double* state_partials(zero_step_state_t* st) {
@@ -181,20 +184,33 @@ int reduce_entry(const char* fn, const void* const* grad_bufs, int32_t n_ranks, 
     zf::ReduceLaunch a;
     memset(&a, 0, sizeof a);
     // vector path: each lane reads 4 consecutive inputs (8 B for 16-bit, 16 B
-    // for fp32) and writes (and, accumulating, reads) 4 fp32 outputs (16 B)
+    // for fp32) and writes (and, accumulating, reads) 4 fp32 outputs (16 B).
+    // Rank slices that all start at one offset within a quad keep it, wherever
+    // they start ("PyTorch FSDP 源码级深度解析" §3.3: rank r's slice starts at
+    // r*S, for any S): the elements up to the first slice's next 128-byte line
+    // go element-wise, then the tiles read whole lines and their reduced quads
+    // are shifted onto the aligned output.
+    const uintptr_t quad = 4 * (uintptr_t)es;
     bool vec = aligned(red_out, 16);
+    uintptr_t mis = 0, line_off = 0;
     for (int32_t k = 0; k < n_ranks; ++k) {
         if (!grad_bufs[k]) return fail(ZERO_EINVAL, "%s: grad_bufs[%d] is NULL", fn, k);
         if (!aligned(grad_bufs[k], es))
             return fail(ZERO_EALIGN, "%s: grad_bufs[%d] misaligned", fn, k);
         const char* p = static_cast<const char*>(grad_bufs[k]) + elem_offset * es;
         a.bufs[k] = p;
-        vec = vec && aligned(p, 4 * es);
+        const uintptr_t m = (uintptr_t)p % quad;
+        if (k == 0) {
+            mis = m;
+            line_off = (uintptr_t)p % kLineBytes;
+        }
+        vec = vec && m == mis;
     }
     a.n_ranks = n_ranks;
     a.dtype = in_dtype;
     a.op = op;
     a.vec = vec ? 1 : 0;
+    a.head = vec && line_off ? (int32_t)((kLineBytes - line_off) / es) : 0;
     a.n = shard_numel;
     a.red_out = red_out;
     a.accumulate = accumulate;
@@ -249,7 +265,11 @@ int zero_unscale_norm(const void* grad_shard, int32_t dtype, int64_t n, zero_ste
     a.n_ranks = 1;
     a.dtype = dtype;
     a.op = ZERO_SUM;
-    a.vec = aligned(grad_shard, 4 * esize(dtype)) ? 1 : 0;
+    // the vector path from the shard's first 128-byte line boundary on (the
+    // head before it element-wise)
+    const uintptr_t line_off = (uintptr_t)grad_shard % kLineBytes;
+    a.vec = 1;
+    a.head = line_off ? (int32_t)((kLineBytes - line_off) / esize(dtype)) : 0;
     a.n = n;
     a.red_out = nullptr;
     a.st = d_state;
@@ -304,11 +324,13 @@ int zero_adamw_shard_step(const void* grad_shard, int32_t grad_dtype, float* mas
     a.lp = static_cast<uint16_t*>(allgather_buf) + slot_offset;
     a.q = quant ? q_buf + q_slot_offset : nullptr;
     a.qs = quant ? q_scales + q_scale_offset : nullptr;
-    // vector path: 16-byte fp32 quads, grad quads of 4*ges bytes, 8-byte slot
-    // quads, 4-byte INT8 quads
-    bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
-               aligned(grad_shard, 4 * ges) && aligned(a.lp, 8);
-    if (quant) vec = vec && aligned(a.q, 4);
+    // vector path: 16-byte fp32 quads and grad quads of 4*ges bytes; the slot
+    // (8-byte quads) and the INT8 codes (4-byte quads) at any element offset:
+    // rank r's slot starts at r*S ("PyTorch FSDP 源码级深度解析" §3.3), and
+    // gfx950 carries out a vector store that is not aligned to its size (the
+    // slot and codes are 3 of the update's 28-31 bytes per parameter)
+    const bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
+                     aligned(grad_shard, 4 * ges);
     a.vec = vec ? 1 : 0;
     a.flags = flags;
     // step scalars formed in double and rounded once to fp32

@@ -371,10 +371,52 @@ struct RawQuad {
     }
 };
 
-template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
+// Shifted slices (SHIFT): the rank slices do not start on a 128-byte line
+// (rank r's slice starts at r*S of its buffer, for any S), while the fp32
+// output is aligned.  The first `head` elements (up to the slices' next line
+// boundary) go element-wise; the tiles then read whole lines of every slice,
+// from element head on.  Tile t's input elements head + t*T + i land on the
+// output at hq + t*T + i + sh, with hq = head - sh a multiple of 4 and
+// sh = head % 4: the reduced quads are computed in the input lane layout and,
+// when sh != 0, one cross-lane shift per chunk turns them into aligned output
+// quads -- output position D takes input position D - sh of its own lane, or
+// D - sh + 4 of the lane below.  Then the output quad at each tile start is
+// shared with the tile below, and each tile writes its part of it (and of
+// the next tile's first quad) element-wise.  Reading partial lines instead
+// (tiles starting at the first quad-aligned element) fetched each tile's edge
+// lines twice: 18% slower on the 8-slice reduce, 40% on the statistics pass.
+// The value lane l - 1 holds (lane 0: its own): one DPP wave shift right by one
+// lane (a gfx9-family DPP control), no LDS crossbar traffic.
+constexpr int kDppWaveShr1 = 0x138;
+__device__ __forceinline__ float from_lane_below(float x) {
+    const int v = __float_as_int(x);
+    return __int_as_float(__builtin_amdgcn_update_dpp(v, v, kDppWaveShr1, 0xf, 0xf, false));
+}
+// The value lane 63 holds, in every lane (a scalar read of one lane).
+__device__ __forceinline__ float from_last_lane(float x) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ uint32_t lane_below_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppWaveShr1, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t last_lane_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+template <int D>
+__device__ __forceinline__ float shift_pick(int sh, const float (&mine)[4], const float (&up)[4]) {
+    const float a1 = D >= 1 ? mine[(D + 3) & 3] : up[3];
+    const float a2 = D >= 2 ? mine[(D + 2) & 3] : up[(D + 2) & 3];
+    const float a3 = D >= 3 ? mine[0] : up[(D + 1) & 3];
+    return sh == 0 ? mine[D] : (sh == 1 ? a1 : (sh == 2 ? a2 : a3));
+}
+
+template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float inv_n,
                                                           int pow2_n, int run_tiles) {
     static_assert(WRITE || !ACC, "accumulation writes its output");
+    static_assert(VEC || !SHIFT, "the shifted layout is a vector layout");
+    static_assert(DT != kQ8 || !SHIFT, "INT8 payload slices are not shifted");
     constexpr int64_t kT = 256 * TU;
     const int lane = threadIdx.x & 63;
     const int64_t wave_id = wave_index();
@@ -394,10 +436,121 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
     // that is the overflow test, taken once per lane after the loop.
     double ss0 = 0.0, ss1 = 0.0;
 
+    // SHIFT: head elements before the slices' first line boundary, their shift
+    // within an output quad and the (quad-aligned) output offset of tile 0
+    const int64_t hs = SHIFT ? a.head : 0;
+    const int sh = (int)(hs & 3);
+    const int64_t hq = hs - sh;
+    // the reduce (AVG applied) of one element from its rank-order sum
+    auto reduced = [&](float sum) -> float {
+        const float q = pow2_n ? sum * inv_n : sum / fN;
+        return avg ? q : sum;
+    };
+    // one element written on its own: value r (reduced), pv its accumulated
+    // value (ACC)
+    auto put_one = [&](int64_t i, float r, float pv) {
+        float val = r;
+        if constexpr (ACC) val = pv + r;
+        if constexpr (WRITE) a.red_out[i] = val;
+        if constexpr (STATS) {
+            const double u = (double)(val * inv_scale);
+            ss0 = __builtin_fma(u, u, ss0);
+        }
+    };
+
+    const int64_t nbody = n > hs ? n - hs : 0;       // elements from the slices' first line boundary on
+    const int64_t ntiles = (nbody + kT - 1) / kT;
+    const int64_t nfull = VEC ? nbody / kT : 0;
+    // SHIFT: lane 63's reduced values of the last chunk of the tile this wave
+    // finished last; when the wave's next tile follows it (inside a run of
+    // consecutive tiles) they complete that tile's first output quad, so the
+    // quads shared between tiles are split only at the ends of a run.
+    float run_carry[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int64_t R = run_tiles;
     // prev: the shard's accumulated values for these elements (ACC only)
     // the quads of the tile at e0 that this lane owns start at e0 + lo + 256 j
     auto finish = [&](const float (&acc)[TU][4], const float (&prev)[TU][4], int64_t e0,
                       uint32_t lo, bool full) {
+        if constexpr (SHIFT) {
+            if (full && !WRITE) {
+                // statistics only: every element of the tile is this lane's, in
+                // the input layout; nothing to place on an output
+#pragma unroll
+                for (int j = 0; j < TU; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const double u = (double)(reduced(acc[j][c]) * inv_scale);
+                        if (c & 2) ss1 = __builtin_fma(u, u, ss1);
+                        else ss0 = __builtin_fma(u, u, ss0);
+                    }
+                return;
+            }
+            if (full) {
+                // acc holds input elements e0 + sh + 256j + lo + c; output quad
+                // (j, lane) is e0 + 256j + lo + d, and prev holds it (ACC);
+                // e0 = hq + t*T
+                const int64_t tt = (e0 - hq) / kT;
+                const bool after = tt % R != 0;                        // the tile below was this wave's
+                const bool before = (tt + 1) % R != 0 && tt + 1 < nfull;  // and so is the next
+                float carry[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) carry[c] = run_carry[c];
+#pragma unroll
+                for (int j = 0; j < TU; ++j) {
+                    float mine[4], up[4], out[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) mine[c] = reduced(acc[j][c]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) up[c] = from_lane_below(mine[c]);
+                    if ((j > 0 || after) && lane == 0) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) up[c] = carry[c];
+                    }
+                    out[0] = shift_pick<0>(sh, mine, up);
+                    out[1] = shift_pick<1>(sh, mine, up);
+                    out[2] = shift_pick<2>(sh, mine, up);
+                    out[3] = shift_pick<3>(sh, mine, up);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) carry[c] = from_last_lane(mine[c]);
+                    const int64_t o0 = e0 + lo + 256 * j;
+                    if (sh != 0 && j == 0 && !after && lane == 0) {
+                        // the first sh elements of this quad belong to another wave's tile
+#pragma unroll
+                        for (int d = 0; d < 4; ++d)
+                            if (d >= sh) put_one(o0 + d, out[d], prev[0][d]);
+                    } else {
+                        float val[4];
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) val[d] = ACC ? prev[j][d] + out[d] : out[d];
+                        stnt_f4(lane_ptr(a.red_out, e0, lo + 256 * j), val[0], val[1], val[2], val[3]);
+                        if constexpr (STATS) {
+#pragma unroll
+                            for (int d = 0; d < 4; ++d) {
+                                const double u = (double)(val[d] * inv_scale);
+                                if (d & 2) ss1 = __builtin_fma(u, u, ss1);
+                                else ss0 = __builtin_fma(u, u, ss0);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) run_carry[c] = carry[c];
+                // the last lane's top elements open the next tile's first quad:
+                // stored here unless this wave finishes that tile next
+                if (!before && lane == 0) {
+#pragma unroll
+                    for (int d = 0; d < 3; ++d) {
+                        if (d < sh) {
+                            const int64_t i = e0 + kT + d;
+                            const int c = d + 4 - sh;
+                            const float r = c == 1 ? carry[1] : (c == 2 ? carry[2] : carry[3]);
+                            put_one(i, r, ACC ? a.red_out[i] : 0.0f);
+                        }
+                    }
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < TU; ++j) {
             const int64_t i0 = e0 + lo + 256 * j;
@@ -430,8 +583,6 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
         }
     };
 
-    const int64_t ntiles = (n + kT - 1) / kT;
-    const int64_t nfull = VEC ? n / kT : 0;
     // ---- full tiles.  A step is one (tile, buffer group) pair.  Wave w walks
     // runs of R consecutive tiles: run w, then run w + nwaves, ...; inside a
     // tile it walks the buffer groups in rank order.
@@ -444,21 +595,21 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
     // two steps run after it.  The compiler then waits for exactly the reads
     // the adds need and keeps the next step's reads (and earlier stores) in
     // flight.
-    const int64_t R = run_tiles;
     if (wave_id * R < nfull) {
         RawQuad<DT> xa[KC][TU], xb[KC][TU];
         RawQuad<ZERO_F32> pa[TU], pb[TU];   // accumulator quads (ACC only)
         const uint32_t lo = 4 * lane;
         auto load_group = [&](RawQuad<DT> (&x)[KC][TU], RawQuad<ZERO_F32> (&px)[TU], int64_t tt,
                               int gg) {
-            const int64_t e0 = tt * kT;
+            const int64_t e0 = tt * kT + hq;              // the output quads' tile start
+            const int64_t ei = tt * kT + hs;              // the inputs' tile start
             int64_t bi[TU];
 #pragma unroll
-            for (int j = 0; j < TU; ++j) bi[j] = DT == kQ8 ? block_of(a, e0 + lo + 256 * j) : 0;
+            for (int j = 0; j < TU; ++j) bi[j] = DT == kQ8 ? block_of(a, ei + lo + 256 * j) : 0;
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk)
 #pragma unroll
-                for (int j = 0; j < TU; ++j) x[kk][j].load(a, gg * KC + kk, e0, lo + 256 * j, bi[j]);
+                for (int j = 0; j < TU; ++j) x[kk][j].load(a, gg * KC + kk, ei, lo + 256 * j, bi[j]);
             if constexpr (ACC) {   // the shard's values, with the group that finishes the tile
                 if (G1 || gg == ngroups - 1) {
 #pragma unroll
@@ -485,7 +636,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
                     prev[j][0] = px[j].x.x; prev[j][1] = px[j].x.y;
                     prev[j][2] = px[j].x.z; prev[j][3] = px[j].x.w;
                 }
-                finish(acc, prev, tt * kT, lo, true);
+                finish(acc, prev, tt * kT + hq, lo, true);
 #pragma unroll
                 for (int j = 0; j < TU; ++j)
 #pragma unroll
@@ -542,9 +693,17 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
             consume(xa, pa, t, g);
         }
     }
+    // ---- the head (SHIFT): the elements before the slices' first line boundary
+    if constexpr (SHIFT) {
+        if (wave_id == 0 && lane < hs && lane < n) {
+            float sum = 0.0f;
+            for (int k = 0; k < N; ++k) sum = sum + RawQuad<DT>::one(a, k, lane);
+            put_one(lane, reduced(sum), ACC ? a.red_out[lane] : 0.0f);
+        }
+    }
     // ---- the ragged tail (or every tile, without the vector path): element-wise
     for (int64_t t = nfull + wave_id; t < ntiles; t += nwaves) {
-        const int64_t base = t * kT + 4 * lane;
+        const int64_t base = hs + t * kT + 4 * lane;
         float acc[TU][4];
 #pragma unroll
         for (int j = 0; j < TU; ++j)
@@ -567,7 +726,7 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
                 const int64_t i = base + 256 * j + c;
                 prev[j][c] = (ACC && i < n) ? a.red_out[i] : 0.0f;
             }
-        finish(acc, prev, t * kT, 4 * lane, false);
+        finish(acc, prev, hs + t * kT, 4 * lane, false);
     }
     if constexpr (STATS) {
         const double mine = ss0 + ss1;
@@ -696,15 +855,29 @@ __device__ __forceinline__ void adam_quad_math(const AdamLaunch& a, const StepSc
 // A full tile: one buffer resource per array over the tile (wave-uniform
 // bases in scalar registers, 32-bit lane offsets); every slice's loads are
 // issued before any arithmetic.
+//
+// The slot and the INT8 codes may start anywhere (rank r's slot sits at r*S
+// of the All-Gather buffer, for any S), while master/m/v and the gradient
+// keep the vector layout.  Then each lane's four 16-bit values (four codes)
+// are joined with the top of the lane below (one DPP wave shift) into the
+// aligned word that covers them, so every store is a whole aligned word; the
+// tile's first word is shared with the tile below and its last elements open
+// the next tile's first word, and those few are stored element by element.
+// Stores of whole 8-byte words at 2-byte offsets instead cost the update 5%.
 template <int GT, int PT, bool QUANT>
 __device__ __forceinline__ void adam_tile_full(const AdamLaunch& a, const StepScalars& s,
                                                int64_t base, int lane) {
     constexpr uint32_t ges = GT == ZERO_F32 ? 4 : 2;
+    uint16_t* const lp = static_cast<uint16_t*>(a.lp);
+    // the slot's (codes') start within an aligned 8-byte (4-byte) word, in elements
+    const int ms = (int)((reinterpret_cast<uintptr_t>(lp) >> 1) & 3);
+    const int mq = QUANT ? (int)(reinterpret_cast<uintptr_t>(a.q) & 3) : 0;
     const BufRes rg = buf_res(static_cast<const char*>(a.g) + base * ges, (uint32_t)(kTile * ges));
     const BufRes rp = buf_res(a.p + base, (uint32_t)(kTile * 4));
     const BufRes rm = buf_res(a.m + base, (uint32_t)(kTile * 4));
     const BufRes rv = buf_res(a.v + base, (uint32_t)(kTile * 4));
-    const BufRes rl = buf_res(static_cast<uint16_t*>(a.lp) + base, (uint32_t)(kTile * 2));
+    // over the aligned words of the tile's slot (codes): word k at byte 8k (4k)
+    const BufRes rl = buf_res(lp + base - ms, (uint32_t)(kTile * 2));
     float gv[kU][4], pv[kU][4], mv[kU][4], vv[kU][4];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -714,6 +887,7 @@ __device__ __forceinline__ void adam_tile_full(const AdamLaunch& a, const StepSc
         bload_quad<ZERO_F32>(rm, e * 4, mv[u]);
         bload_quad<ZERO_F32>(rv, e * 4, vv[u]);
     }
+    uint32_t carry_lo = 0, carry_hi = 0, carry_q = 0;   // lane 63's words of the slice before
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const uint32_t e = 256 * u + 4 * lane;
@@ -723,14 +897,54 @@ __device__ __forceinline__ void adam_tile_full(const AdamLaunch& a, const StepSc
         bstore_f4(rp, e * 4, pv[u]);
         bstore_f4(rm, e * 4, mv[u]);
         bstore_f4(rv, e * 4, vv[u]);
-        v2u w;
-        w.x = lp16[0] | (lp16[1] << 16);
-        w.y = lp16[2] | (lp16[3] << 16);
-        bst_u2(rl, e * 2, w);
+        const uint32_t wlo = lp16[0] | (lp16[1] << 16), whi = lp16[2] | (lp16[3] << 16);
+        if (ms == 0) {
+            v2u w;
+            w.x = wlo;
+            w.y = whi;
+            bst_u2(rl, e * 2, w);
+        } else {
+            uint32_t blo = lane_below_u(wlo), bhi = lane_below_u(whi);
+            if (lane == 0) {
+                blo = carry_lo;
+                bhi = carry_hi;
+            }
+            const uint64_t mine = (uint64_t)wlo | ((uint64_t)whi << 32);
+            const uint64_t below = (uint64_t)blo | ((uint64_t)bhi << 32);
+            const uint64_t x = (mine << (16 * ms)) | (below >> (64 - 16 * ms));
+            carry_lo = last_lane_u(wlo);
+            carry_hi = last_lane_u(whi);
+            if (u == 0 && lane == 0) {      // the word shared with the tile below
+                for (int c = 0; c < 4 - ms; ++c) lp[base + c] = (uint16_t)lp16[c];
+            } else {
+                v2u w;
+                w.x = (uint32_t)x;
+                w.y = (uint32_t)(x >> 32);
+                bst_u2(rl, e * 2, w);
+            }
+            if (u == kU - 1 && lane == 63) {   // the start of the next tile's first word
+                for (int c = 4 - ms; c < 4; ++c) lp[base + e + c] = (uint16_t)lp16[c];
+            }
+        }
         if constexpr (QUANT) {
             float scale;
             const uint32_t q = quant_quad(lpv, &scale);  // whole wave takes part
-            bst_u1(buf_res(a.q + base, (uint32_t)kTile), e, q);
+            if (mq == 0) {
+                bst_u1(buf_res(a.q + base, (uint32_t)kTile), e, q);
+            } else {
+                uint32_t b = lane_below_u(q);
+                if (lane == 0) b = carry_q;
+                const uint32_t x = (q << (8 * mq)) | (b >> (32 - 8 * mq));
+                carry_q = last_lane_u(q);
+                if (u == 0 && lane == 0) {
+                    for (int c = 0; c < 4 - mq; ++c) a.q[base + c] = (int8_t)(q >> (8 * c));
+                } else {
+                    bst_u1(buf_res(a.q + base - mq, (uint32_t)kTile), e, x);
+                }
+                if (u == kU - 1 && lane == 63) {
+                    for (int c = 4 - mq; c < 4; ++c) a.q[base + e + c] = (int8_t)(q >> (8 * c));
+                }
+            }
             if (lane == 0) a.qs[(base + 256 * u) / 256] = scale;
         }
     }
@@ -1128,7 +1342,7 @@ int grid_for_tiles(int64_t ntiles, int cap) {
 // the state's per-block partial sums (ZERO_MAX_PARTIALS).
 constexpr int64_t kRunSteps = 16;
 constexpr int64_t kFillBlocks = 4096;
-template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
+template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
 void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
     const int64_t ntiles = (a.n + 256 * TU - 1) / (256 * TU);
     const int64_t ngroups = G1 ? 1 : a.n_ranks / KC;
@@ -1140,17 +1354,17 @@ void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int po
     if (run < need) run = need;
     int64_t grid = (ntiles + kWaves * run - 1) / (kWaves * run);
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((reduce_kernel<DT, VEC, WRITE, STATS, TU, KC, ACC, G1>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((reduce_kernel<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, G1>), dim3((unsigned)grid),
                        dim3(kThreads), 0, (hipStream_t)stream, a, inv_n, pow2, (int)run);
 }
 
-template <int DT, bool VEC, bool WRITE, bool STATS, int TU, int KC, bool ACC>
+template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, int TU, int KC, bool ACC>
 void launch_reduce_shape(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
-    if (a.n_ranks == KC) launch_reduce_grid<DT, VEC, WRITE, STATS, TU, KC, ACC, true>(a, stream, inv_n, pow2);
-    else launch_reduce_grid<DT, VEC, WRITE, STATS, TU, KC, ACC, false>(a, stream, inv_n, pow2);
+    if (a.n_ranks == KC) launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, true>(a, stream, inv_n, pow2);
+    else launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, false>(a, stream, inv_n, pow2);
 }
 
-template <int DT, bool VEC, bool WRITE, bool STATS, bool ACC>
+template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, bool ACC>
 int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     const int N = a.n_ranks;
     const int pow2 = (N & (N - 1)) == 0;
@@ -1159,12 +1373,12 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     // 16-bit or fp32 buffers read one chunk of 16 buffers per step (7% faster
     // than two chunks of 8 at 64 buffers); INT8 payloads keep two chunks of 8.
     if (DT != kQ8 && N % 16 == 0)
-        launch_reduce_shape<DT, VEC, WRITE, STATS, 1, 16, ACC>(a, stream, inv_n, pow2);
-    else if (N % 8 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
-    else if (N % 4 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
-    else if (N % 2 == 0) launch_reduce_shape<DT, VEC, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
-    else if (N == 1) launch_reduce_shape<DT, VEC, WRITE, STATS, 2, 1, ACC>(a, stream, inv_n, pow2);
-    else launch_reduce_shape<DT, VEC, WRITE, STATS, 8, 1, ACC>(a, stream, inv_n, pow2);
+        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 1, 16, ACC>(a, stream, inv_n, pow2);
+    else if (N % 8 == 0) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
+    else if (N % 4 == 0) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
+    else if (N % 2 == 0) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
+    else if (N == 1) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 1, ACC>(a, stream, inv_n, pow2);
+    else launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 8, 1, ACC>(a, stream, inv_n, pow2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (STATS) {
@@ -1175,29 +1389,30 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     return (int)e;
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool SHIFT>
 int launch_reduce_d(const ReduceLaunch& a, void* stream) {
     const bool write = a.red_out != nullptr;
     const bool stats = a.st != nullptr;
     if (write && a.accumulate) {
-        if (stats) return launch_reduce_t<DT, VEC, true, true, true>(a, stream);
-        return launch_reduce_t<DT, VEC, true, false, true>(a, stream);
+        if (stats) return launch_reduce_t<DT, VEC, SHIFT, true, true, true>(a, stream);
+        return launch_reduce_t<DT, VEC, SHIFT, true, false, true>(a, stream);
     }
-    if (write && stats) return launch_reduce_t<DT, VEC, true, true, false>(a, stream);
-    if (write) return launch_reduce_t<DT, VEC, true, false, false>(a, stream);
-    return launch_reduce_t<DT, VEC, false, true, false>(a, stream);
+    if (write && stats) return launch_reduce_t<DT, VEC, SHIFT, true, true, false>(a, stream);
+    if (write) return launch_reduce_t<DT, VEC, SHIFT, true, false, false>(a, stream);
+    return launch_reduce_t<DT, VEC, SHIFT, false, true, false>(a, stream);
 }
 
 template <int DT>
 int launch_reduce_v(const ReduceLaunch& a, void* stream) {
-    return a.vec ? launch_reduce_d<DT, true>(a, stream) : launch_reduce_d<DT, false>(a, stream);
+    if (!a.vec) return launch_reduce_d<DT, false, false>(a, stream);
+    return a.head ? launch_reduce_d<DT, true, true>(a, stream) : launch_reduce_d<DT, true, false>(a, stream);
 }
 
 // quantised payload: always writes the fp32 shard; statistics optional
 template <bool VEC>
 int launch_reduce_q8_v(const ReduceLaunch& a, void* stream) {
-    if (a.st) return launch_reduce_t<kQ8, VEC, true, true, false>(a, stream);
-    return launch_reduce_t<kQ8, VEC, true, false, false>(a, stream);
+    if (a.st) return launch_reduce_t<kQ8, VEC, false, true, true, false>(a, stream);
+    return launch_reduce_t<kQ8, VEC, false, true, false, false>(a, stream);
 }
 
 template <int GT, int PT, bool QUANT>

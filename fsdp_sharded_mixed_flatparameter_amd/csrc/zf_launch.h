@@ -16,7 +16,11 @@ struct ReduceLaunch {
     int32_t n_ranks;
     int32_t dtype;   // zero_dtype_t of the inputs
     int32_t op;      // zero_reduce_op_t
-    int32_t vec;     // 1: every pointer allows 16-byte accesses
+    int32_t vec;     // 1: vector path (every pointer allows quad accesses, from
+                     // element `head` on for the inputs)
+    int32_t head;    // vector path: elements 0 .. head-1 precede the inputs' first
+                     // 128-byte line boundary (0..63; the output is 16-byte
+                     // aligned at element 0)
     int64_t n;
     float* red_out;  // may be null
     int32_t accumulate;     // 1: red_out += reduce (red_out is read, then written)
