@@ -83,6 +83,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the other workloads")
+    ap.add_argument("--only", default="",
+                    help="comma-separated workloads to run alone (10b_n8 for the headline, a "
+                         "variant, 10b_n8_reduce8_shift1, tiny_mlp_n4_graph, offload or a "
+                         "gather), for per-workload profiles; the line then holds just those")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="accepted for older command lines: the calibration kernels (the "
                          "counters' copy reference and the ceilings) now always run")
@@ -677,7 +681,63 @@ def main():
     from synth.workloads import WORKLOADS
     w = WORKLOADS["10b_n8"]
     S = w.shard
+    only = [x for x in args.only.split(",") if x]
 
+    def sel(name):
+        return not only or name in only
+
+    if sel("10b_n8"):
+        out = run_headline(zf, torch, w, args)
+    else:
+        out = {"only": only}
+    if not args.no_variants:
+        out["variants"] = {}
+        for name, what in VARIANTS:
+            if not sel(name):
+                continue
+            r = run_workload(zf, torch, WORKLOADS[name], max(3, args.steps // 2), 2,
+                             flush=name in FLUSHED)
+            r["what"] = what
+            if not args.no_cpu_baseline:
+                r["cpu_baseline"] = cpu_baseline_workload(torch, WORKLOADS[name],
+                                                          *CPU_SAMPLES[name])
+                r["cpu_baseline"]["gpu_over_oracle"] = r["params_per_s"] / r["cpu_baseline"]["value"]
+            out["variants"][name] = r
+        # the same steps with every rank slice and the slot one element off
+        # the vector boundary (rank r's slice starts at r*S for any S)
+        for name, base in (("10b_n8_reduce8_shift1", "10b_n8_reduce8"),):
+            if not sel(name):
+                continue
+            r = run_workload(zf, torch, WORKLOADS[base], max(3, args.steps // 2), 2, shift=1)
+            r["what"] = ("as %s, with every rank slice starting 1 element into its buffer and "
+                         "the slot 1 element past its place: the reduce's shifted vector path "
+                         "and the update's joined slot words" % base)
+            if base in out["variants"]:
+                r["vs_aligned"] = out["variants"][base]["ms_per_step"] / r["ms_per_step"]
+            out["variants"][name] = r
+        if sel("tiny_mlp_n4_graph"):
+            out["variants"]["tiny_mlp_n4_graph"] = run_graph(
+                zf, torch, WORKLOADS["tiny_mlp_n4"], max(20, args.steps), 5)
+        if sel("offload"):
+            out["offload"] = run_offload(zf, torch, w, 3, 1)
+        from synth.workloads import GATHERS
+        out["allgather_consumer"] = {}
+        for name, what in GATHER_VARIANTS:
+            if not sel(name):
+                continue
+            r = run_gather(zf, torch, GATHERS[name], max(3, args.steps // 4), 1)
+            r["what"] = what
+            out["allgather_consumer"][name] = r
+    if not args.no_cpu_baseline and sel("10b_n8"):
+        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"]["gpu_over_oracle"] = out["value"] / out["cpu_baseline"]["value"]
+    print(json.dumps(out), flush=True)
+
+
+def run_headline(zf, torch, w, args):
+    """The headline line: the 10B/8 step over N_ALLOC fresh allocations, with
+    the ceilings measured in the same process."""
+    S = w.shard
     ceilings = run_ceilings(torch)
     # the headline over N_ALLOC fresh allocations of the step's arrays: where
     # they land in physical memory moves every streaming kernel on them
@@ -751,39 +811,7 @@ def main():
                      "frac_of_step_array_copy": achieved / ceilings["copy_step_arrays"]["GBps"]},
         "ceilings": ceilings,
     }
-    if not args.no_variants:
-        out["variants"] = {}
-        for name, what in VARIANTS:
-            r = run_workload(zf, torch, WORKLOADS[name], max(3, args.steps // 2), 2,
-                             flush=name in FLUSHED)
-            r["what"] = what
-            if not args.no_cpu_baseline:
-                r["cpu_baseline"] = cpu_baseline_workload(torch, WORKLOADS[name],
-                                                          *CPU_SAMPLES[name])
-                r["cpu_baseline"]["gpu_over_oracle"] = r["params_per_s"] / r["cpu_baseline"]["value"]
-            out["variants"][name] = r
-        # the same steps with every rank slice and the slot one element off
-        # the vector boundary (rank r's slice starts at r*S for any S)
-        for name, base in (("10b_n8_reduce8_shift1", "10b_n8_reduce8"),):
-            r = run_workload(zf, torch, WORKLOADS[base], max(3, args.steps // 2), 2, shift=1)
-            r["what"] = ("as %s, with every rank slice starting 1 element into its buffer and "
-                         "the slot 1 element past its place: the reduce's shifted vector path "
-                         "and an unaligned slot" % base)
-            r["vs_aligned"] = out["variants"][base]["ms_per_step"] / r["ms_per_step"]
-            out["variants"][name] = r
-        out["variants"]["tiny_mlp_n4_graph"] = run_graph(zf, torch, WORKLOADS["tiny_mlp_n4"],
-                                                         max(20, args.steps), 5)
-        out["offload"] = run_offload(zf, torch, w, 3, 1)
-        from synth.workloads import GATHERS
-        out["allgather_consumer"] = {}
-        for name, what in GATHER_VARIANTS:
-            r = run_gather(zf, torch, GATHERS[name], max(3, args.steps // 4), 1)
-            r["what"] = what
-            out["allgather_consumer"][name] = r
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
-        out["cpu_baseline"]["gpu_over_oracle"] = out["value"] / out["cpu_baseline"]["value"]
-    print(json.dumps(out), flush=True)
+    return out
 
 
 if __name__ == "__main__":
