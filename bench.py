@@ -546,7 +546,8 @@ def run_gather(zf, torch, g, steps, warmup):
 
 
 def run_offload(zf, torch, w, steps, warmup):
-    """ZeRO-Offload on the same shard: statistics on the GPU, the fp16 gradient
+    """ZeRO-Offload on the same shard (the median of `steps` steps): statistics
+    on the GPU, the fp16 gradient
     to pinned host memory in chunks, the update on host cores over host-resident
     fp32 master/m/v, the fp16 parameters back into the All-Gather slot.  Also
     the host link's own rates (pinned 2.5 GB copies each way) and the host
@@ -572,10 +573,13 @@ def run_offload(zf, torch, w, steps, warmup):
     torch.cuda.synchronize()
     for _ in range(warmup):
         opt.step_from_reduced(g, ag, w.start)
-    t0 = time.perf_counter()
+    # each step returns when its copies and the device finalize are done
+    per_step = []
     for _ in range(steps):
+        t0 = time.perf_counter()
         opt.step_from_reduced(g, ag, w.start)
-    wall = (time.perf_counter() - t0) / steps
+        per_step.append(time.perf_counter() - t0)
+    wall = sorted(per_step)[len(per_step) // 2]       # the median step
     st = opt.state.read()
     assert st.last_skipped == 0 and st.step == warmup + steps
     # the host update alone (no copies), same threads, same arrays
@@ -613,7 +617,8 @@ def run_offload(zf, torch, w, steps, warmup):
     del opt, g, ag, master, buf, stage, lp_out
     torch.cuda.empty_cache()
     host_bytes = 2 + 12 + 12 + 2                  # grad read, master/m/v read+write, fp16 write
-    return {"ms_per_step": wall * 1e3, "params_per_s": S / wall, "host_threads": threads,
+    return {"ms_per_step": wall * 1e3, "ms_each_step": [t * 1e3 for t in per_step],
+            "params_per_s": S / wall, "host_threads": threads,
             "host_link_bytes_per_param": 4, "host_link_GBps": 4 * S / wall / 1e9,
             "host_link_ceiling_GBps": rates, "host_bytes_per_param": host_bytes,
             "host_GBps": host_bytes * S / wall / 1e9, "host_copy_ceiling_GBps": host_copy,
@@ -719,7 +724,7 @@ def main():
             out["variants"]["tiny_mlp_n4_graph"] = run_graph(
                 zf, torch, WORKLOADS["tiny_mlp_n4"], max(20, args.steps), 5)
         if sel("offload"):
-            out["offload"] = run_offload(zf, torch, w, 3, 1)
+            out["offload"] = run_offload(zf, torch, w, 5, 2)
         from synth.workloads import GATHERS
         out["allgather_consumer"] = {}
         for name, what in GATHER_VARIANTS:
