@@ -547,11 +547,11 @@ def run_gather(zf, torch, g, steps, warmup):
 
 def run_offload(zf, torch, w, steps, warmup):
     """ZeRO-Offload on the same shard (the median of `steps` steps): statistics
-    on the GPU, the fp16 gradient
-    to pinned host memory in chunks, the update on host cores over host-resident
-    fp32 master/m/v, the fp16 parameters back into the All-Gather slot.  Also
-    the host link's own rates (pinned 2.5 GB copies each way) and the host
-    threads' streaming rate, the two ceilings of this step."""
+    on the GPU, the fp16 gradient to pinned host memory in chunks, the update
+    on host cores over host-resident fp32 master/m/v, the fp16 parameters back
+    into the All-Gather slot.  Also the host link's own rates (pinned 2.5 GB
+    copies each way) and the host threads' streaming rate, the two ceilings of
+    this step."""
     from synth import synth
     from synth.workloads import key_grad_reduced, key_master
     S = w.shard
