@@ -270,7 +270,10 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // partials[block] (the state's table, or the library's device scratch) and an
 // overflow flag.  A fold kernel adds the partials into st->sumsq in a fixed
 // order, so the sum is reproducible.  The partials bound the grid (at most
-// ZERO_MAX_PARTIALS blocks).
+// ZERO_MAX_PARTIALS blocks); a shard that needs more blocks is reduced in
+// several launches over consecutive tile ranges, block b of every later
+// launch adding its sum onto partials[b], so the fold still sees one fixed
+// order.
 //
 // Mapping (quad, as the AdamW kernel): in chunk j of a tile, lane l owns
 // elements 256j + 4l .. 4l+3, so every wave instruction covers one contiguous
@@ -278,10 +281,12 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // that leaves half of each cache line to another instruction costs about a
 // third of the bandwidth here.
 //
-// Work split: wave w walks runs of R consecutive tiles, run w, then run
-// w + nwaves, ...  The launcher sizes the grid so that each wave has one run
-// (about 16 steps), unless the shard needs more blocks than the state holds
-// partials.
+// Work split: a launch covers full tiles [tile0, tile_end); wave w walks runs
+// of R consecutive tiles from tile0 + w*R, then w*R + nwaves*R, ...  The
+// launcher picks R (one tile per wave for the 16-bit and fp32 inputs, runs of
+// about 16 steps for INT8 payloads) and sizes the grid so that each wave has
+// one run.  The first launch of a shard also does the head elements, the last
+// one the ragged tail.
 //
 // Pipelining: a wave walks (tile, group of KC buffers) pairs in order and
 // issues the reads of the next pair before adding the current one and before
@@ -296,6 +301,11 @@ __device__ __forceinline__ StepScalars read_step(const zero_step_state_t* st, do
 // Reduce-Scatter payload), rank k's codes at bufs[2k] and scales at bufs[2k+1];
 // its value is f32(code) * scale, one binary32 product.
 constexpr int kQ8 = 3;
+
+// reduce launch parts (the `part` argument)
+constexpr int kPartFirst = 1;   // does the head elements (the shard's first launch)
+constexpr int kPartLast = 2;    // does the ragged tail (its last launch)
+constexpr int kPartAdd = 4;     // adds onto the partials of the launch before
 
 __device__ __forceinline__ int64_t block_of(const ReduceLaunch& a, int64_t i) {
     return a.block_shift >= 0 ? (i >> a.block_shift) : i / a.block;
@@ -413,7 +423,9 @@ __device__ __forceinline__ float shift_pick(int sh, const float (&mine)[4], cons
 
 template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
 __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float inv_n,
-                                                          int pow2_n, int run_tiles) {
+                                                          int pow2_n, int run_tiles,
+                                                          int64_t tile0, int64_t tile_end,
+                                                          int part) {
     static_assert(WRITE || !ACC, "accumulation writes its output");
     static_assert(VEC || !SHIFT, "the shifted layout is a vector layout");
     static_assert(DT != kQ8 || !SHIFT, "INT8 payload slices are not shifted");
@@ -490,8 +502,8 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
                 // (j, lane) is e0 + 256j + lo + d, and prev holds it (ACC);
                 // e0 = hq + t*T
                 const int64_t tt = (e0 - hq) / kT;
-                const bool after = tt % R != 0;                        // the tile below was this wave's
-                const bool before = (tt + 1) % R != 0 && tt + 1 < nfull;  // and so is the next
+                const bool after = (tt - tile0) % R != 0;                  // the tile below was this wave's
+                const bool before = (tt + 1 - tile0) % R != 0 && tt + 1 < tile_end;  // and so is the next
                 float carry[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) carry[c] = run_carry[c];
@@ -595,7 +607,8 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
     // two steps run after it.  The compiler then waits for exactly the reads
     // the adds need and keeps the next step's reads (and earlier stores) in
     // flight.
-    if (wave_id * R < nfull) {
+    const int64_t wt0 = tile0 + wave_id * R;            // this wave's first full tile
+    if (wt0 < tile_end) {
         RawQuad<DT> xa[KC][TU], xb[KC][TU];
         RawQuad<ZERO_F32> pa[TU], pb[TU];   // accumulator quads (ACC only)
         const uint32_t lo = 4 * lane;
@@ -646,11 +659,11 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
         // this wave's full tiles: runs start at w*R + j*nwaves*R; every run
         // but the last holds R tiles
         const int64_t span = nwaves * R;
-        const int64_t q = nfull - wave_id * R;           // > 0 here
+        const int64_t q = tile_end - wt0;                 // > 0 here
         const int64_t runs = (q + span - 1) / span;
         const int64_t last = q - (runs - 1) * span;
         const int64_t nsteps = ((runs - 1) * R + (last < R ? last : R)) * ngroups;
-        int64_t t = wave_id * R, left = R;
+        int64_t t = wt0, left = R;
         int g = 0;
         auto advance = [&]() {   // (t, g) := the step after (t, g)
             ++g;
@@ -695,14 +708,14 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
     }
     // ---- the head (SHIFT): the elements before the slices' first line boundary
     if constexpr (SHIFT) {
-        if (wave_id == 0 && lane < hs && lane < n) {
+        if ((part & kPartFirst) && wave_id == 0 && lane < hs && lane < n) {
             float sum = 0.0f;
             for (int k = 0; k < N; ++k) sum = sum + RawQuad<DT>::one(a, k, lane);
             put_one(lane, reduced(sum), ACC ? a.red_out[lane] : 0.0f);
         }
     }
     // ---- the ragged tail (or every tile, without the vector path): element-wise
-    for (int64_t t = nfull + wave_id; t < ntiles; t += nwaves) {
+    for (int64_t t = nfull + wave_id; (part & kPartLast) && t < ntiles; t += nwaves) {
         const int64_t base = hs + t * kT + 4 * lane;
         float acc[TU][4];
 #pragma unroll
@@ -733,8 +746,12 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
         const int ovf = !isfinite(mine);
         const double bs = block_sum(mine);
         if (threadIdx.x == 0) {
-            a.partials[blockIdx.x] = bs;
-            if (blockIdx.x == 0) a.st->n_partials = (int32_t)gridDim.x;
+            if (part & kPartAdd) {
+                a.partials[blockIdx.x] = a.partials[blockIdx.x] + bs;
+            } else {
+                a.partials[blockIdx.x] = bs;
+                if (blockIdx.x == 0) a.st->n_partials = (int32_t)gridDim.x;
+            }
         }
         if (__ballot(ovf) != 0ull && lane == 0) atomicOr(&a.st->overflow, 1);
     }
@@ -1336,26 +1353,64 @@ int grid_for_tiles(int64_t ntiles, int cap) {
 // hardware dispatcher issues the blocks in order, so the tiles in flight at
 // any moment form one narrow window of each buffer.  (A persistent grid whose
 // waves walk the shard measured 5-10% slower: its waves drift apart and the
-// reads in flight spread over the buffers.)  R aims at kRunSteps steps per
-// wave (a step is one tile of one buffer group), shrinks so that small shards
-// still launch kFillBlocks blocks, and grows when the blocks would outnumber
-// the state's per-block partial sums (ZERO_MAX_PARTIALS).
+// reads in flight spread over the buffers.)  A reduce of 16-bit or fp32
+// inputs takes one tile per wave (R = 1): on 8 fp16 slices of 1.25e9 elements
+// that measured 7-10% faster than runs of 16 tiles, whose waves work in as
+// many separate windows.  With statistics a launch has at most
+// ZERO_MAX_PARTIALS blocks, so a larger shard is reduced by several launches
+// over consecutive tile ranges, each later one adding its blocks' sums onto
+// the partials; R grows only when that would take more than kMaxLaunches.
+// INT8 payloads and the statistics-only pass keep runs of about kRunSteps
+// steps (a step is one tile of one buffer group; R shrinks so that small
+// shards still launch kFillBlocks blocks and grows so that the blocks fit the
+// partial sums): one launch, at 98% of the read-only rate for the latter.
 constexpr int64_t kRunSteps = 16;
 constexpr int64_t kFillBlocks = 4096;
+constexpr int64_t kMaxLaunches = 8;
+constexpr int64_t kMaxGridPlain = int64_t(1) << 30;   // no partial sums to hold
 template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
 void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
-    const int64_t ntiles = (a.n + 256 * TU - 1) / (256 * TU);
+    constexpr int64_t kT = 256 * TU;
+    const int64_t hs = SHIFT ? a.head : 0;           // as the kernel splits the shard
+    const int64_t nbody = a.n > hs ? a.n - hs : 0;
+    const int64_t ntiles = (nbody + kT - 1) / kT;
+    const int64_t nfull = VEC ? nbody / kT : 0;
     const int64_t ngroups = G1 ? 1 : a.n_ranks / KC;
-    int64_t run = kRunSteps / ngroups;
-    const int64_t fill = ntiles / (kWaves * kFillBlocks);
-    if (run > fill) run = fill;
-    if (run < 1) run = 1;
-    const int64_t need = (ntiles + kWaves * kMaxGridReduce - 1) / (kWaves * kMaxGridReduce);
-    if (run < need) run = need;
-    int64_t grid = (ntiles + kWaves * run - 1) / (kWaves * run);
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((reduce_kernel<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, G1>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, (hipStream_t)stream, a, inv_n, pow2, (int)run);
+    const int64_t cap = STATS ? kMaxGridReduce : kMaxGridPlain;
+    int64_t run;
+    if (DT == kQ8 || !WRITE) {
+        run = kRunSteps / ngroups;
+        const int64_t fill = ntiles / (kWaves * kFillBlocks);
+        if (run > fill) run = fill;
+        if (run < 1) run = 1;
+        const int64_t need = (ntiles + kWaves * cap - 1) / (kWaves * cap);
+        if (run < need) run = need;
+    } else {
+        const int64_t span = kWaves * cap * kMaxLaunches;   // tiles at R = 1
+        run = (nfull + span - 1) / span;
+        if (run < 1) run = 1;
+    }
+    const int64_t per_block = kWaves * run;          // full tiles per block
+    const int64_t chunk = cap * per_block;           // full tiles per launch
+    int64_t t0 = 0;
+    int part = kPartFirst;
+    for (;;) {
+        const int64_t t1 = nfull - t0 > chunk ? t0 + chunk : nfull;
+        const bool last = t1 == nfull;
+        int64_t grid = (t1 - t0 + per_block - 1) / per_block;
+        if (last) {   // the ragged tail's tiles go to the last launch's waves
+            int64_t tail = (ntiles - nfull + kWaves - 1) / kWaves;
+            if (tail > cap) tail = cap;
+            if (grid < tail) grid = tail;
+        }
+        if (grid < 1) grid = 1;
+        hipLaunchKernelGGL((reduce_kernel<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, G1>),
+                           dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, a, inv_n,
+                           pow2, (int)run, t0, t1, part | (last ? kPartLast : 0));
+        if (last) break;
+        t0 = t1;
+        part = kPartAdd;
+    }
 }
 
 template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, int TU, int KC, bool ACC>
@@ -1371,9 +1426,14 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     const float inv_n = 1.0f / (float)N;  // exact when N is a power of two
     // reads in flight per lane: TU chunks x KC buffers (KC divides N).  Many
     // 16-bit or fp32 buffers read one chunk of 16 buffers per step (7% faster
-    // than two chunks of 8 at 64 buffers); INT8 payloads keep two chunks of 8.
+    // than two chunks of 8 at 64 buffers); eight 16-bit buffers read four
+    // chunks of all eight (a whole tile in one step, 4-8% faster than two
+    // chunks); INT8 payloads keep two chunks of 8.
+    constexpr bool k16 = DT == ZERO_F16 || DT == ZERO_BF16;
     if (DT != kQ8 && N % 16 == 0)
         launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 1, 16, ACC>(a, stream, inv_n, pow2);
+    else if (k16 && N == 8)
+        launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, (k16 ? 4 : 2), 8, ACC, true>(a, stream, inv_n, pow2);
     else if (N % 8 == 0) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
     else if (N % 4 == 0) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
     else if (N % 2 == 0) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
@@ -1459,8 +1519,9 @@ int launch_reduce_stats(const ReduceLaunch& a, void* stream) {
 // The statistics' per-block partial sums for zero_grad_reduce_shard_noalloc,
 // for callers that cannot allocate: one array per device, held until the
 // process ends.  Every such call on a device shares it (calls that overlap on
-// one device race); each launch writes every partial it later folds, so
-// nothing needs clearing between calls.
+// one device race); the first launch of a reduce writes every partial its fold
+// reads (later launches of the same reduce add onto them), so nothing needs
+// clearing between calls.
 static __device__ __align__(256) double scratch[ZERO_MAX_PARTIALS];
 
 namespace zf {

@@ -206,16 +206,16 @@ int zero_grad_reduce_shard(const void* const* grad_bufs, int32_t n_ranks, int32_
  * static array of ZERO_MAX_PARTIALS doubles (512 KiB) per device, held until
  * the process ends -- instead of d_state->partials.  d_state (when not NULL)
  * then needs only its first ZERO_STEP_STATE_HEADER_BYTES bytes; the library
- * neither reads nor writes the partials table of the caller's state.  A
- * launch never needs more partial sums than the array holds, at any shard
- * size (each wave's run of tiles lengthens instead), so no size is refused on
- * its account; the other limits are zero_grad_reduce_shard's.  The call
+ * neither reads nor writes the partials table of the caller's state.  No
+ * shard size is refused on the array's account (a large shard is reduced by
+ * several launches whose blocks add onto the same partial sums, or by longer
+ * runs of tiles per wave); the other limits are zero_grad_reduce_shard's.  The call
  * allocates nothing, host or device: the array's device address is looked up
  * once per device, on the first call made with that device current.  Every
  * such call on one device shares the array, so calls that overlap in time on
  * one device (two streams, or two host threads) race and must be ordered by
- * the caller; each launch writes every partial sum it folds, so nothing
- * carries over from one call to the next. */
+ * the caller; the first launch of each call writes every partial sum its
+ * fold reads, so nothing carries over from one call to the next. */
 #define ZERO_STEP_STATE_HEADER_BYTES ((int64_t)offsetof(zero_step_state_t, partials))
 int zero_grad_reduce_shard_noalloc(const void* const* grad_bufs, int32_t n_ranks,
                                    int32_t in_dtype, int64_t elem_offset, int64_t shard_numel,

@@ -1,19 +1,22 @@
-"""Reduce parity at sizes where every wave runs the pipelined loop over a run
-of several tiles: whole outputs compared element by element with the oracle
-(not samples).  The launcher gives each wave one run of R tiles (about 16
-steps of one tile and one buffer group each, fewer when the shard is small),
-so these sizes reach, per case:
+"""Reduce parity at sizes where every wave runs the pipelined loop, whole
+outputs compared element by element with the oracle (not samples).  A
+reduce of 16-bit or fp32 buffers gives each wave one tile, whose steps (one
+buffer group each) the loop pipelines; INT8 payloads and the statistics
+pass give each wave a run of R tiles (about 16 steps, fewer when the shard
+is small).  Per case:
 
-  8 fp16 buffers, 60,500,123 elements   one group, R = 7 (odd step count)
-  32 bf16 buffers, 10,000,257           two groups of 16, R = 2 (4 steps)
+  8 fp16 buffers, 60,500,123 elements   one step of four chunks per wave
+  32 bf16 buffers, 10,000,257           two groups of 16 (2 steps)
   12 fp16 buffers, 20,000,263, 2 micro-steps accumulated
-                                        three groups, R = 2 (6 steps)
+                                        three groups of 4 (3 steps)
   8 INT8 payloads, 45,200,000           one group, R = 5
-  4 fp16 buffers, 135,000,000           one group, R = 16 (the full run)
-  2 fp32 buffers, 53,000,003            one group of two, R = 3
+  4 fp16 buffers, 135,000,000           65,918 blocks: two launches, the
+                                        second adding onto the first's
+                                        65,536 partial sums
+  2 fp32 buffers, 53,000,003            one group of two
   statistics pass, 80,000,001 fp16      one buffer, R = 9
 
-and in each the last wave's run is cut short by the end of the full tiles,
+and in each the last wave's work is cut short by the end of the full tiles,
 followed by the ragged tail.  Bar: the reduced (or accumulated) shard bit for
 bit; the overflow flag exact; the sum of squares within n * 2^-53 relative:
 the oracle adds the n non-negative terms one after another in binary64, which
