@@ -61,6 +61,27 @@ constexpr int kMaxGridStream = 1 << 22;
 constexpr int kMaxGridStep = ZF_ADAM_GRID > 0 ? ZF_ADAM_GRID : kMaxGridStream;
 constexpr int kMaxGridReduce = ZERO_MAX_PARTIALS;
 
+// Launch slices and an occupancy cap for the long streaming kernels.  One
+// launch of a few hundred thousand blocks streams a little slower than the
+// same tiles issued as consecutive launches of kSliceBlocks blocks (tile
+// ranges [t0, t1), same stream): on the 1.25e9-element update 6.24-6.38 ms
+// as one launch against 5.90-5.96 ms in slices of 16,384 blocks, and the
+// 8-slice reduce and the INT8 gather gained 4-6% the same way.  A kernel
+// boundary makes every XCD finish before the next range starts, which keeps
+// the addresses in flight in one window; within one long launch the
+// dispatch order alone does not.  kLdsTwoBlocks is a dynamic LDS reservation
+// (unused by the kernel) that lets only two 256-thread blocks reside per
+// compute unit (160 KiB of LDS): the update and the wide reduces, whose
+// waves each keep 16-32 KiB of reads in flight, ran another 1-5% faster so;
+// kernels with fewer bytes in flight per wave (the statistics pass, the
+// INT8 quantiser and gather) ran 30-70% slower and keep full occupancy, and
+// so do launches of fewer than kTwoBlocksMin blocks (the 7B block's reduce,
+// 6,200 blocks, ran 1-2% slower with the cap) and the update with the INT8
+// epilogue (on the 70B shard 5.85 against 5.35 ms in slices without it).
+constexpr int64_t kSliceBlocks = 32768;
+constexpr unsigned kLdsTwoBlocks = 56 * 1024;
+constexpr int64_t kTwoBlocksMin = 8192;
+
 // Native vectors for the non-temporal (streaming, read-once / write-once)
 // accesses: every array of the step is touched exactly once per launch.
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -1014,7 +1035,7 @@ __device__ __forceinline__ void adam_tile_part(const AdamLaunch& a, const StepSc
 }
 
 template <int GT, int PT, bool QUANT, bool VEC>
-__global__ void __launch_bounds__(kThreads) adamw_kernel(AdamLaunch a) {
+__global__ void __launch_bounds__(kThreads) adamw_kernel(AdamLaunch a, int64_t t0, int64_t t1) {
     const StepScalars s = read_step(a.st, a.beta1, a.beta2, a.max_norm);
     if (s.skip) return;  // overflow on this or another rank: nothing is written
     const int lane = threadIdx.x & 63;
@@ -1022,7 +1043,7 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamLaunch a) {
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const int64_t ntiles = (a.n + kTile - 1) / kTile;
     const int64_t nfull = VEC ? a.n / kTile : 0;
-    for (int64_t t = wave_id; t < ntiles; t += nwaves) {
+    for (int64_t t = t0 + wave_id; t < t1 && t < ntiles; t += nwaves) {
         if (t < nfull) adam_tile_full<GT, PT, QUANT>(a, s, t * kTile, lane);
         else adam_tile_part<GT, PT, QUANT>(a, s, t * kTile, lane);
     }
@@ -1292,7 +1313,8 @@ __global__ void __launch_bounds__(kThreads) dequant_kernel(DequantLaunch a, int 
 // the quad path (slot_numel % 4 == 0: a lane quad never straddles a slot or a
 // block).
 template <int OT>
-__global__ void __launch_bounds__(kThreads) dequant_flat_kernel(DequantLaunch a, int block_shift) {
+__global__ void __launch_bounds__(kThreads) dequant_flat_kernel(DequantLaunch a, int block_shift,
+                                                                int64_t t0, int64_t t1) {
     const int lane = threadIdx.x & 63;
     const int64_t wave_id = wave_index();
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
@@ -1304,7 +1326,7 @@ __global__ void __launch_bounds__(kThreads) dequant_flat_kernel(DequantLaunch a,
     auto block_of = [&](int64_t i) -> int64_t {
         return block_shift >= 0 ? (i >> block_shift) : i / a.block;
     };
-    for (int64_t t = wave_id; t < ntiles; t += nwaves) {
+    for (int64_t t = t0 + wave_id; t < t1 && t < ntiles; t += nwaves) {
         const int64_t e0 = t * kDTile;
         const int64_t s0 = e0 / S;          // slot of the tile's first element
         const int64_t b1 = (s0 + 1) * S;    // first element of the next slot
@@ -1356,17 +1378,17 @@ int grid_for_tiles(int64_t ntiles, int cap) {
 // reads in flight spread over the buffers.)  A reduce of 16-bit or fp32
 // inputs takes one tile per wave (R = 1): on 8 fp16 slices of 1.25e9 elements
 // that measured 7-10% faster than runs of 16 tiles, whose waves work in as
-// many separate windows.  With statistics a launch has at most
-// ZERO_MAX_PARTIALS blocks, so a larger shard is reduced by several launches
-// over consecutive tile ranges, each later one adding its blocks' sums onto
-// the partials; R grows only when that would take more than kMaxLaunches.
+// many separate windows.  It is issued as launches of at most kSliceBlocks
+// blocks over consecutive tile ranges; with statistics every later launch
+// adds its blocks' sums onto the partials the first one wrote.  R grows only
+// when the shard would take more than kMaxLaunches launches.
 // INT8 payloads and the statistics-only pass keep runs of about kRunSteps
 // steps (a step is one tile of one buffer group; R shrinks so that small
 // shards still launch kFillBlocks blocks and grows so that the blocks fit the
 // partial sums): one launch, at 98% of the read-only rate for the latter.
 constexpr int64_t kRunSteps = 16;
 constexpr int64_t kFillBlocks = 4096;
-constexpr int64_t kMaxLaunches = 8;
+constexpr int64_t kMaxLaunches = 64;
 constexpr int64_t kMaxGridPlain = int64_t(1) << 30;   // no partial sums to hold
 template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
 void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
@@ -1376,7 +1398,14 @@ void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int po
     const int64_t ntiles = (nbody + kT - 1) / kT;
     const int64_t nfull = VEC ? nbody / kT : 0;
     const int64_t ngroups = G1 ? 1 : a.n_ranks / KC;
-    const int64_t cap = STATS ? kMaxGridReduce : kMaxGridPlain;
+    // reduces of 16-bit and fp32 inputs go in launch slices; INT8 payloads
+    // and the statistics pass in one launch (fewer blocks than partials)
+    const bool sliced = DT != kQ8 && WRITE;
+    const int64_t cap = sliced ? kSliceBlocks : (STATS ? kMaxGridReduce : kMaxGridPlain);
+    static_assert(kSliceBlocks <= kMaxGridReduce, "a launch slice holds one partial per block");
+    // two blocks per compute unit for the shapes with TU x KC >= 16 quads
+    // in flight per lane
+    const bool two = WRITE && TU * KC >= 16;
     int64_t run;
     if (DT == kQ8 || !WRITE) {
         run = kRunSteps / ngroups;
@@ -1404,8 +1433,9 @@ void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int po
             if (grid < tail) grid = tail;
         }
         if (grid < 1) grid = 1;
+        const unsigned lds = two && grid >= kTwoBlocksMin ? kLdsTwoBlocks : 0u;
         hipLaunchKernelGGL((reduce_kernel<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, G1>),
-                           dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, a, inv_n,
+                           dim3((unsigned)grid), dim3(kThreads), lds, (hipStream_t)stream, a, inv_n,
                            pow2, (int)run, t0, t1, part | (last ? kPartLast : 0));
         if (last) break;
         t0 = t1;
@@ -1478,13 +1508,18 @@ int launch_reduce_q8_v(const ReduceLaunch& a, void* stream) {
 template <int GT, int PT, bool QUANT>
 int launch_adamw_q(const AdamLaunch& a, void* stream) {
     const int64_t ntiles = (a.n + kTile - 1) / kTile;
-    const int grid = grid_for_tiles(ntiles, kMaxGridStep);
-    if (a.vec)
-        hipLaunchKernelGGL((adamw_kernel<GT, PT, QUANT, true>), dim3(grid), dim3(kThreads), 0,
-                           (hipStream_t)stream, a);
-    else
-        hipLaunchKernelGGL((adamw_kernel<GT, PT, QUANT, false>), dim3(grid), dim3(kThreads), 0,
-                           (hipStream_t)stream, a);
+    const int64_t slice = kSliceBlocks * kWaves;   // tiles per launch
+    for (int64_t t0 = 0; t0 < ntiles; t0 += slice) {
+        const int64_t t1 = ntiles - t0 < slice ? ntiles : t0 + slice;
+        const int grid = grid_for_tiles(t1 - t0, kMaxGridStep);
+        const unsigned lds = !QUANT && grid >= kTwoBlocksMin ? kLdsTwoBlocks : 0u;
+        if (a.vec)
+            hipLaunchKernelGGL((adamw_kernel<GT, PT, QUANT, true>), dim3(grid), dim3(kThreads),
+                               lds, (hipStream_t)stream, a, t0, t1);
+        else
+            hipLaunchKernelGGL((adamw_kernel<GT, PT, QUANT, false>), dim3(grid), dim3(kThreads), 0,
+                               (hipStream_t)stream, a, t0, t1);
+    }
     return (int)hipGetLastError();
 }
 
@@ -1592,13 +1627,20 @@ int launch_dequant(const DequantLaunch& a, void* stream) {
     const int64_t ntiles = flat ? (a.slot_numel * a.n_slots + kDTile - 1) / kDTile
                                 : per_slot * a.n_slots;
     const int grid = grid_for_tiles(ntiles, kMaxGridStream);
+    const int64_t slice = kSliceBlocks * kWaves;   // flat tiles per launch
     int shift = -1;
     if ((a.block & (a.block - 1)) == 0) shift = __builtin_ctz((unsigned)a.block);
     hipStream_t s = (hipStream_t)stream;
 #define ZF_DQ(OT)                                                                           \
     do {                                                                                    \
-        if (flat) hipLaunchKernelGGL((dequant_flat_kernel<OT>), dim3(grid), dim3(kThreads), 0, s, a, shift); \
-        else if (a.vec) hipLaunchKernelGGL((dequant_kernel<OT, true>), dim3(grid), dim3(kThreads), 0, s, a, shift); \
+        if (flat) {                                                                         \
+            for (int64_t t0 = 0; t0 < ntiles; t0 += slice) {                                \
+                const int64_t t1 = ntiles - t0 < slice ? ntiles : t0 + slice;              \
+                hipLaunchKernelGGL((dequant_flat_kernel<OT>),                                \
+                                   dim3(grid_for_tiles(t1 - t0, kMaxGridStream)), dim3(kThreads), \
+                                   0, s, a, shift, t0, t1);                                 \
+            }                                                                               \
+        } else if (a.vec) hipLaunchKernelGGL((dequant_kernel<OT, true>), dim3(grid), dim3(kThreads), 0, s, a, shift); \
         else hipLaunchKernelGGL((dequant_kernel<OT, false>), dim3(grid), dim3(kThreads), 0, s, a, shift);      \
     } while (0)
     if (a.out_dtype == ZERO_F32) ZF_DQ(ZERO_F32);

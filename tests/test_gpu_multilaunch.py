@@ -1,8 +1,9 @@
-"""GPU parity of a reduce that takes several launches: with the step statistics
-each launch holds at most ZERO_MAX_PARTIALS blocks, so a shard of more than
-that many blocks' tiles (2^28 elements of eight 16-bit slices) is reduced over
-consecutive tile ranges, each later launch adding its block sums onto the
-same partials.  The whole reduced shard is compared with the oracle bit for
+"""GPU parity of a reduce that takes several launches: a reduce of 16-bit
+slices is issued as launches of at most 32,768 blocks (4 tiles of 1,024
+elements each for eight slices) over consecutive tile ranges, and with the
+step statistics each later launch adds its block sums onto the partials the
+first one wrote.  Shards of 2^28 elements and more take three launches or
+more.  The whole reduced shard is compared with the oracle bit for
 bit (ZeRO's Reduce-Scatter, "PyTorch FSDP 源码级深度解析" §3.3: every element
 of the rank's slice is the rank-order reduce), the sum of squares within
 n * 2^-53 relative; the no-allocation entry point must give the same bits.
@@ -44,12 +45,12 @@ def rel(a, b):
     return abs(a - b) / max(abs(b), 1e-300)
 
 
-# (dtype, op, shard elements, slice offset, accumulate): more than
-# 65536 blocks x 4 tiles x 1024 elements, so at least two launches
+# (dtype, op, shard elements, slice offset, accumulate): more than twice
+# 32768 blocks x 4 tiles x 1024 elements (2^27), so three launches or more
 CASES = [
     (orc.F16, 1, (1 << 28) + 5_000, 0, False),
     (orc.F16, 1, (1 << 28) + 1_000_003, 1, False),    # slices one element into a line
-    (orc.BF16, 0, 3 * (1 << 28) + 77, 3, False),       # three launches, SUM
+    (orc.BF16, 0, 3 * (1 << 28) + 77, 3, False),       # six launches and the tail, SUM
     (orc.F16, 1, (1 << 28) + 4099, 2, True),           # accumulation with statistics
 ]
 
@@ -117,7 +118,7 @@ def test_reduce_over_several_launches(zf, dt, op, n, off, acc):
     assert st.overflow == 0 and not any(p[1] for p in parts)
     assert rel(st.sumsq, s_ref) <= n * 2.0 ** -53, (st.sumsq, s_ref)
     say("  sumsq", st.sumsq, "oracle", s_ref, "partials", st.n_partials)
-    assert st.n_partials == 65536          # the first launch's full grid
+    assert st.n_partials == 32768          # the first launch's full grid
     if not acc:
         out2, st2 = run(True)
         assert_bitwise(to_host(out2), got, "no-allocation reduce")

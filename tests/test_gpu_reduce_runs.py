@@ -10,9 +10,9 @@ is small).  Per case:
   12 fp16 buffers, 20,000,263, 2 micro-steps accumulated
                                         three groups of 4 (3 steps)
   8 INT8 payloads, 45,200,000           one group, R = 5
-  4 fp16 buffers, 135,000,000           65,918 blocks: two launches, the
-                                        second adding onto the first's
-                                        65,536 partial sums
+  4 fp16 buffers, 135,000,000           65,918 blocks: three launches,
+                                        the later two adding onto the
+                                        first's 32,768 partial sums
   2 fp32 buffers, 53,000,003            one group of two
   statistics pass, 80,000,001 fp16      one buffer, R = 9
 
