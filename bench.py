@@ -305,21 +305,24 @@ def run_prereduced(zf, torch, w, steps, warmup):
     n = S // 1024 * 1024
     slot = ag[w.start:w.start + n]
     from synth import synth as _s
-    mix_ms = _event_ms(torch, lambda: _s.mix28(grads[0][:n], opt.master[:n], opt.exp_avg[:n],
-                                               opt.exp_avg_sq[:n], slot), 5)
+    mix_ms, mix_forms = _best_form(torch, lambda: _s.mix28(grads[0][:n], opt.master[:n],
+                                                           opt.exp_avg[:n], opt.exp_avg_sq[:n],
+                                                           slot), 5)
     res["mix"] = dict(bytes_per_launch=28 * n, ms_per_launch=mix_ms,
                       GBps=28 * n / (mix_ms * 1e-3) / 1e9,
+                      GBps_by_form={k: 28 * n / (v * 1e-3) / 1e9 for k, v in mix_forms.items()},
                       what="the update's byte mix (fp16 g, fp32 p/m/v, fp16 copy of p; trivial "
                            "arithmetic, same lane layout) on the step's own arrays, after the "
-                           "timed steps")
+                           "timed steps, fastest launch form")
     # and a plain copy between two of them (master into exp_avg; the state is
     # not used again): every streaming kernel on these arrays moves with their
     # physical placement, so this is the ceiling the update is compared with
-    copy_ms = _event_ms(torch, lambda: _s.copy(opt.master, opt.exp_avg), 5)
+    copy_ms, copy_forms = _best_form(torch, lambda: _s.copy(opt.master, opt.exp_avg), 5)
     res["copy"] = dict(bytes_per_launch=8 * S, ms_per_launch=copy_ms,
                        GBps=8 * S / (copy_ms * 1e-3) / 1e9,
+                       GBps_by_form={k: 8 * S / (v * 1e-3) / 1e9 for k, v in copy_forms.items()},
                        what="plain non-temporal 16-byte copy of the fp32 master into exp_avg "
-                            "(the step's own arrays), after the timed steps")
+                            "(the step's own arrays), after the timed steps, fastest launch form")
     del opt, grads, ag, master
     torch.cuda.empty_cache()
     return res
@@ -648,12 +651,32 @@ def _event_ms(torch, fn, reps):
     return ms[len(ms) // 2]
 
 
+# launch forms of the calibration streams: one launch, the library's launch
+# slices of 32,768 blocks, and those slices with two resident blocks per
+# compute unit (56 KiB of dynamic LDS reserved); a stream's ceiling is the
+# fastest form
+SLICE_BLOCKS, LDS_TWO_BLOCKS = 32768, 56 * 1024
+LAUNCH_FORMS = (("one_launch", 0, 0), ("slices", SLICE_BLOCKS, 0),
+                ("slices_two_blocks_per_cu", SLICE_BLOCKS, LDS_TWO_BLOCKS))
+
+
+def _best_form(torch, fn, reps):
+    """ms of fn in each launch form; (best ms, {form: ms})."""
+    from synth import synth
+    forms = {}
+    for name, sl, lds in LAUNCH_FORMS:
+        with synth.launch_form(sl, lds):
+            forms[name] = _event_ms(torch, fn, reps)
+    return min(forms.values()), forms
+
+
 def run_ceilings(torch, nbytes=4 << 30, reps=5):
     """The practical HBM ceilings of this machine, measured in the same process as
     the step with the streaming calibration kernels of synth (non-temporal
     16-byte accesses, HIP events on the launch stream): read-only, write-only
-    and copy (its dispatches also calibrate the rocprofv3 byte counters).  The
-    fused update's own byte mix is measured by run_prereduced on its arrays."""
+    and copy, each in every launch form, the fastest kept (the one-launch
+    copy's dispatches also calibrate the rocprofv3 byte counters).  The fused
+    update's own byte mix is measured by run_prereduced on its arrays."""
     from synth import synth
     out = {}
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -664,12 +687,15 @@ def run_ceilings(torch, nbytes=4 << 30, reps=5):
     for name, fn, moved in (("read", lambda: synth.read_stream(a, sink), nbytes),
                             ("write", lambda: synth.write_stream(b), nbytes),
                             ("copy", lambda: synth.copy(a, b), 2 * nbytes)):
-        ms = _event_ms(torch, fn, reps)
-        out[name] = dict(bytes_per_launch=moved, ms_per_launch=ms, GBps=moved / (ms * 1e-3) / 1e9)
+        ms, forms = _best_form(torch, fn, reps)
+        out[name] = dict(bytes_per_launch=moved, ms_per_launch=ms, GBps=moved / (ms * 1e-3) / 1e9,
+                         GBps_by_form={k: moved / (v * 1e-3) / 1e9 for k, v in forms.items()})
     del a, b
     torch.cuda.empty_cache()
-    out["what"] = ("synth calibration kernels, same process, read/write/copy over %d MiB; adamw_mix "
-                   "runs on the step's own arrays" % (nbytes >> 20))
+    out["what"] = ("synth calibration kernels, same process, read/write/copy over %d MiB, the "
+                   "fastest of: one launch, launches of %d blocks, those with two blocks per "
+                   "compute unit; adamw_mix runs on the step's own arrays"
+                   % (nbytes >> 20, SLICE_BLOCKS))
     return out
 
 

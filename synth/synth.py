@@ -84,6 +84,8 @@ def _gpu_lib():
         L.synth_write.argtypes = [C.c_void_p, C.c_int64, C.c_uint32, C.c_void_p]
         L.synth_mix28.restype = C.c_int
         L.synth_mix28.argtypes = [C.c_void_p] * 5 + [C.c_int64, C.c_void_p]
+        L.synth_set_launch_form.restype = C.c_int
+        L.synth_set_launch_form.argtypes = [C.c_int64, C.c_uint32]
         _gpu = L
     return _gpu
 
@@ -225,3 +227,22 @@ def mix28(g, p, m, v, lp, stream=None):
                                 _stream(stream))
     if rc != 0:
         raise RuntimeError("synth_mix28 failed: hip error %d" % rc)
+
+class launch_form:
+    """Context manager: issue the calibration streams (read, write, copy without
+    a grid, mix28) as consecutive launches of at most `slice_blocks` blocks, each
+    with `lds_bytes` of dynamic LDS reserved (caps the resident blocks per
+    compute unit); the library's streaming kernels use such launch forms."""
+
+    def __init__(self, slice_blocks=0, lds_bytes=0):
+        self.form = (slice_blocks, lds_bytes)
+
+    def __enter__(self):
+        rc = _gpu_lib().synth_set_launch_form(*self.form)
+        if rc != 0:
+            raise RuntimeError("synth_set_launch_form failed: hip error %d" % rc)
+        return self
+
+    def __exit__(self, *exc):
+        _gpu_lib().synth_set_launch_form(0, 0)
+        return False

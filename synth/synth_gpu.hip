@@ -215,16 +215,49 @@ int synth_fill_codes(uint64_t key, int64_t start, int64_t n, int8_t* out, void* 
     return (int)hipGetLastError();
 }
 
+/* Launch form of the calibration streams below (copy without an explicit
+ * grid, read, write, mix28): 0 = one launch; else consecutive launches of at
+ * most slice_blocks blocks over consecutive spans (tiles), each with lds_bytes
+ * of dynamic LDS reserved (unused; it caps the blocks resident per compute
+ * unit).  The same forms as the library's streaming kernels, so that their
+ * ceilings are measured in the launch form the kernels use. */
+static int64_t g_slice_blocks = 0;
+static unsigned g_lds_bytes = 0;
+
+int synth_set_launch_form(int64_t slice_blocks, uint32_t lds_bytes) {
+    if (slice_blocks < 0 || lds_bytes > 80u * 1024u) return (int)hipErrorInvalidValue;
+    g_slice_blocks = slice_blocks;
+    g_lds_bytes = lds_bytes;
+    return 0;
+}
+
+// spans of 1024 16-byte words per launch (all of them in one launch by default)
+// (at most 2^22 blocks of 256 threads per launch: HIP's 2^32-thread grid limit)
+static int64_t spans_per_launch(int64_t spans) {
+    int64_t per = g_slice_blocks > 0 && g_slice_blocks < spans ? g_slice_blocks : spans;
+    return per > (1 << 22) ? (1 << 22) : per;
+}
+
 int synth_copy(const void* src, void* dst, int64_t nbytes, int32_t grid, void* stream) {
     if (nbytes <= 0) return 0;
     if ((nbytes & 15) || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
         return (int)hipErrorInvalidValue;
     const int64_t n16 = nbytes / 16;
     int64_t spans = (n16 + 1023) / 1024;
-    if (spans > (1 << 22)) spans = 1 << 22;
-    const int g = grid > 0 ? grid : (int)spans;
-    hipLaunchKernelGGL(copy16, dim3(g), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
-                       (u32x4*)dst, n16);
+    if (grid > 0 || spans > (1 << 22)) {   // one launch, blocks looping over spans
+        if (spans > (1 << 22)) spans = 1 << 22;
+        const int g = grid > 0 ? grid : (int)spans;
+        hipLaunchKernelGGL(copy16, dim3(g), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
+                           (u32x4*)dst, n16);
+        return (int)hipGetLastError();
+    }
+    const int64_t per = spans_per_launch(spans);
+    for (int64_t s0 = 0; s0 < spans; s0 += per) {
+        const int64_t w0 = s0 * 1024;
+        const int64_t nw = n16 - w0 < per * 1024 ? n16 - w0 : per * 1024;
+        hipLaunchKernelGGL(copy16, dim3((int)((nw + 1023) / 1024)), dim3(256), g_lds_bytes,
+                           (hipStream_t)stream, (const u32x4*)src + w0, (u32x4*)dst + w0, nw);
+    }
     return (int)hipGetLastError();
 }
 
@@ -234,10 +267,15 @@ int synth_read(const void* src, int64_t nbytes, void* sink, void* stream) {
     if (nbytes <= 0) return 0;
     if ((nbytes & 15) || ((uintptr_t)src & 15)) return (int)hipErrorInvalidValue;
     const int64_t n16 = nbytes / 16;
-    int64_t spans = (n16 + 1023) / 1024;
-    if (spans > (1 << 22)) spans = 1 << 22;
-    hipLaunchKernelGGL(read16, dim3((int)spans), dim3(256), 0, (hipStream_t)stream,
-                       (const u32x4*)src, n16, 0x9e3779b9u, (uint32_t*)sink);
+    const int64_t spans = (n16 + 1023) / 1024;
+    const int64_t per = spans_per_launch(spans);
+    for (int64_t s0 = 0; s0 < spans; s0 += per) {
+        const int64_t w0 = s0 * 1024;
+        const int64_t nw = n16 - w0 < per * 1024 ? n16 - w0 : per * 1024;
+        hipLaunchKernelGGL(read16, dim3((int)((nw + 1023) / 1024)), dim3(256), g_lds_bytes,
+                           (hipStream_t)stream, (const u32x4*)src + w0, nw, 0x9e3779b9u,
+                           (uint32_t*)sink);
+    }
     return (int)hipGetLastError();
 }
 
@@ -246,10 +284,14 @@ int synth_write(void* dst, int64_t nbytes, uint32_t val, void* stream) {
     if (nbytes <= 0) return 0;
     if ((nbytes & 15) || ((uintptr_t)dst & 15)) return (int)hipErrorInvalidValue;
     const int64_t n16 = nbytes / 16;
-    int64_t spans = (n16 + 1023) / 1024;
-    if (spans > (1 << 22)) spans = 1 << 22;
-    hipLaunchKernelGGL(write16, dim3((int)spans), dim3(256), 0, (hipStream_t)stream, (u32x4*)dst,
-                       n16, val);
+    const int64_t spans = (n16 + 1023) / 1024;
+    const int64_t per = spans_per_launch(spans);
+    for (int64_t s0 = 0; s0 < spans; s0 += per) {
+        const int64_t w0 = s0 * 1024;
+        const int64_t nw = n16 - w0 < per * 1024 ? n16 - w0 : per * 1024;
+        hipLaunchKernelGGL(write16, dim3((int)((nw + 1023) / 1024)), dim3(256), g_lds_bytes,
+                           (hipStream_t)stream, (u32x4*)dst + w0, nw, val);
+    }
     return (int)hipGetLastError();
 }
 
@@ -263,8 +305,14 @@ int synth_mix28(const void* g, float* p, float* m, float* v, void* lp, int64_t n
     const int64_t ntiles = n / 1024;
     const int64_t blocks = (ntiles + 3) / 4;
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(mix28, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                       (const uint16_t*)g, p, m, v, (uint16_t*)lp, ntiles);
+    const int64_t per = 4 * spans_per_launch(blocks);   // tiles per launch
+    for (int64_t t0 = 0; t0 < ntiles; t0 += per) {
+        const int64_t nt = ntiles - t0 < per ? ntiles - t0 : per;
+        const int64_t e0 = t0 * 1024;
+        hipLaunchKernelGGL(mix28, dim3((unsigned)((nt + 3) / 4)), dim3(256), g_lds_bytes,
+                           (hipStream_t)stream, (const uint16_t*)g + e0, p + e0, m + e0, v + e0,
+                           (uint16_t*)lp + e0, nt);
+    }
     return (int)hipGetLastError();
 }
 
