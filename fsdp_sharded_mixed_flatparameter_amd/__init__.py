@@ -114,10 +114,12 @@ def lib():
     return _lib
 
 
+_DTYPE_CODES = {"float32": ZERO_F32, "float16": ZERO_F16, "bfloat16": ZERO_BF16}
+
+
 def _dtype_code(t):
-    import torch
     try:
-        return {torch.float32: ZERO_F32, torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16}[t.dtype]
+        return _DTYPE_CODES[_dtype_name(t.dtype)]
     except KeyError:
         raise ValueError("unsupported dtype %s" % t.dtype) from None
 
@@ -126,10 +128,20 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+def _current_raw_stream():
+    """torch's current HIP stream on the current device, as an integer handle
+    (the raw-stream query torch's own generated code uses; the public
+    torch.cuda.current_stream() costs several microseconds per call)."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is None:
+        return torch.cuda.current_stream().cuda_stream
+    return raw(torch._C._cuda_getDevice())
+
+
 def _stream(stream):
     if stream is None:
-        import torch
-        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return C.c_void_p(_current_raw_stream())
     if hasattr(stream, "cuda_stream"):
         return C.c_void_p(stream.cuda_stream)
     return C.c_void_p(int(stream))
@@ -145,12 +157,22 @@ _F16_BF16 = ("float16", "bfloat16")
 _FLOATS = ("float32", "float16", "bfloat16")
 
 
+_DTYPE_NAMES = {}
+
+
+def _dtype_name(dt):
+    name = _DTYPE_NAMES.get(dt)
+    if name is None:
+        name = _DTYPE_NAMES[dt] = str(dt).replace("torch.", "")
+    return name
+
+
 def _dev(t, name, dtypes=None):
     """A device argument: a contiguous CUDA tensor of one of `dtypes` (names)."""
     _contig(t, name)
     if not t.is_cuda:
         raise ValueError("%s must be a device (CUDA) tensor" % name)
-    if dtypes is not None and str(t.dtype).replace("torch.", "") not in dtypes:
+    if dtypes is not None and _dtype_name(t.dtype) not in dtypes:
         raise ValueError("%s must be %s, not %s" % (name, " or ".join(dtypes), t.dtype))
     return t
 

@@ -5,9 +5,9 @@ arithmetic happens here; every part of the step runs in libzeroflat.
 """
 import torch
 
-from . import (ZERO_AVG, StepState, zero_adamw_shard_step, zero_grad_accumulate_shard,
-               zero_grad_reduce_shard, zero_grad_reduce_shard_int8, zero_offload_step,
-               zero_unscale_norm)
+from . import (ZERO_AVG, StepState, _current_raw_stream, zero_adamw_hparams_t,
+               zero_adamw_shard_step, zero_grad_accumulate_shard, zero_grad_reduce_shard,
+               zero_grad_reduce_shard_int8, zero_offload_step, zero_unscale_norm)
 
 
 class ShardOptimizer:
@@ -22,10 +22,18 @@ class ShardOptimizer:
         self.state = StepState(loss_scale, dynamic, window, min_scale, device=master.device)
         self.quant_block = quant_block
         self._red = None
+        self._h = (None, None)   # (hp items, their C struct)
 
     @property
     def numel(self):
         return self.master.numel()
+
+    def _hparams(self):
+        """The C hyper-parameter struct, rebuilt only when self.hp changed."""
+        key = tuple(self.hp.items())
+        if self._h[0] != key:
+            self._h = (key, zero_adamw_hparams_t(**self.hp))
+        return self._h[1]
 
     def reduced_buffer(self):
         if self._red is None:
@@ -37,6 +45,8 @@ class ShardOptimizer:
                                q_scale_offset=0, stream=None):
         """Reduce-Scatter's reduce over the N rank buffers, then the step."""
         red = self.reduced_buffer()
+        if stream is None:
+            stream = _current_raw_stream()   # one lookup for both calls
         zero_grad_reduce_shard(grad_bufs, elem_offset, self.numel, op, red, self.state,
                                stream=stream)
         self._apply(red, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
@@ -48,6 +58,8 @@ class ShardOptimizer:
         """Reduce over the N ranks' INT8-quantised gradient slices for this rank
         (ZeRO++'s quantised Reduce-Scatter), then the step."""
         red = self.reduced_buffer()
+        if stream is None:
+            stream = _current_raw_stream()
         zero_grad_reduce_shard_int8(q_slices, scale_slices, self.numel, op, red, self.state,
                                     block=block, stream=stream)
         self._apply(red, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
@@ -77,6 +89,8 @@ class ShardOptimizer:
     def step_from_reduced(self, grad_shard, allgather_buf, slot_offset, q_buf=None,
                           q_scales=None, q_slot_offset=0, q_scale_offset=0, stream=None):
         """Statistics over an already reduced (fp32/fp16/bf16) shard, then the step."""
+        if stream is None:
+            stream = _current_raw_stream()
         zero_unscale_norm(grad_shard, self.state, n=self.numel, stream=stream)
         self._apply(grad_shard, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
                     q_scale_offset, stream)
@@ -84,7 +98,8 @@ class ShardOptimizer:
     def _apply(self, grad, allgather_buf, slot_offset, q_buf, q_scales, q_slot_offset,
                q_scale_offset, stream):
         zero_adamw_shard_step(grad, self.master, self.exp_avg, self.exp_avg_sq, allgather_buf,
-                              slot_offset, self.hp, self.state, q_buf=q_buf, q_scales=q_scales,
+                              slot_offset, self._hparams(), self.state, q_buf=q_buf,
+                              q_scales=q_scales,
                               q_slot_offset=q_slot_offset, q_scale_offset=q_scale_offset,
                               q_block=self.quant_block or 256, finalize=True, stream=stream)
 
