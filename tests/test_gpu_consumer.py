@@ -135,10 +135,40 @@ def test_llama7b_block_gather_full_size(zf):
     torch.cuda.empty_cache()
 
 
+def test_gather_over_several_launches(zf):
+    """A flat output of 3 x 200,000,004 elements: the vector path issues it as
+    launches of 32,768 blocks (268,435,456 elements each) over consecutive
+    tile ranges, three here, with slot boundaries inside tiles.  Every element
+    against the oracle (codes and scales generated on the GPU, host copies
+    checked against the host generator at sampled indices)."""
+    n_slots, S, block = 3, 200_000_004, 256
+    nb = -(-S // block)
+    say("gather over launches", n_slots, S)
+    q = torch.empty(n_slots * S, dtype=torch.int8, device="cuda")
+    kq, ks = synth.stream_key("dq-launch", "codes"), synth.stream_key("dq-launch", "scales")
+    synth.fill_codes(q, kq)
+    sc = torch.empty(n_slots * nb, device="cuda")
+    synth.fill_normal(sc, ks, 0, 4.7e-6)
+    sc.abs_()
+    out = torch.empty(n_slots * S, dtype=torch.bfloat16, device="cuda")
+    zf.zero_dequant_allgather(q, sc, n_slots, S, out, block=block)
+    qh, sh = to_host(q), to_host(sc).copy()
+    rng = np.random.default_rng(11)
+    idx = np.unique(rng.integers(0, n_slots * S, 20_000))
+    assert_bitwise(qh[idx].view(np.uint8), synth.codes_at(kq, idx).view(np.uint8), "codes copy")
+    sidx = np.unique(rng.integers(0, sh.size, 2_000))
+    assert_bitwise(sh[sidx], np.abs(synth.normal_f32_at(ks, sidx, 4.7e-6)), "scales copy")
+    ref = orc.dequant_int8(qh, sh, n_slots, S, block, orc.BF16)
+    assert_bitwise(to_host(out), ref, "flat buffer over three launches")
+    del q, sc, out
+    torch.cuda.empty_cache()
+
+
 def test_70b_n64_gather_full_size(zf):
     """The whole 70B flat parameter (7e10 bf16) from 64 slots: 2^20 random
-    elements plus 2,048 elements on each side of every slot boundary and the
-    last (short) block of every slot, each against the oracle."""
+    elements plus 2,048 elements on each side of every slot boundary and of
+    every launch slice (261 launches), and the last (short) block of every
+    slot, each against the oracle."""
     g = GATHERS["70b_n64_gather"]
     torch.cuda.empty_cache()
     free, _ = torch.cuda.mem_get_info()
@@ -153,6 +183,9 @@ def test_70b_n64_gather_full_size(zf):
     rng = np.random.default_rng(7)
     S = g.shard
     parts = [rng.integers(0, g.padded, 1 << 20)]
+    slice_elems = 32768 * 4 * 2048     # the elements of one launch slice
+    for b in range(slice_elems, g.padded, slice_elems):
+        parts.append(np.arange(b - 2048, min(g.padded, b + 2048)))
     for s in range(g.n_ranks):
         parts.append(np.arange(max(0, s * S - 2048), min(g.padded, s * S + 2048)))
         parts.append(np.arange((s + 1) * S - (S - (g.n_blocks - 1) * g.block), (s + 1) * S))
