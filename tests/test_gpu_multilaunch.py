@@ -126,3 +126,66 @@ def test_reduce_over_several_launches(zf, dt, op, n, off, acc):
         del out2
     del bufs, out, host, acc0
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("vector", [True, False])
+def test_adamw_over_several_launches(zf, vector):
+    """The fused AdamW step over 2 x 131,072 tiles + 777 elements: launches of
+    32,768 blocks (4 tiles of 1,024 elements each) over consecutive tile
+    ranges, three here.  With `vector` False the master shard starts 4 bytes
+    past a 16-byte boundary, which sends every tile down the element-wise
+    path, in the same launch ranges.  Two steps, every element of master, m,
+    v and the fp16 slot against the oracle; clipping active."""
+    n = 2 * 131072 * 1024 + 777
+    say("adamw over launches", n, "vector" if vector else "element-wise")
+    dev = torch.device("cuda:0")
+    hp = dict(lr=3e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.5)
+    scale = 1024.0
+    kp = synth.stream_key("multi-adam-p", n)
+    base = torch.empty(n + (0 if vector else 1), device=dev)
+    master = base if vector else base[1:]
+    synth.fill_normal(master, kp, 0, 0.02)
+    p = to_host(master).copy()
+    opt = zf.ShardOptimizer(master, hp, loss_scale=scale, dynamic=False)
+    assert (master.data_ptr() % 16 == 0) == vector
+    ag = torch.zeros(n, dtype=torch.float16, device=dev)
+    g = torch.empty(n, dtype=torch.float16, device=dev)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    hpo = orc.Hparams(**hp)
+    for step in range(2):
+        kg = synth.stream_key("multi-adam-g", n, step)
+        synth.fill_normal(g, kg, 0, 1e-3 * scale)
+        gh = to_host(g).copy()
+        idx = np.unique(np.random.default_rng(step).integers(0, n, 5_000))
+        assert_bitwise(gh[idx], synth.normal_at(kg, idx, 1e-3 * scale, orc.F16), "grad copy")
+        opt.step_from_reduced(g, ag, 0)
+        st = opt.state.read()
+
+        def stats(lo):
+            return orc.unscale_stats(np.ascontiguousarray(gh[lo:lo + CHUNK]), orc.F16, scale)
+
+        with ThreadPoolExecutor(THREADS) as ex:
+            sumsq = sum(s for s, _ in ex.map(stats, range(0, n, CHUNK)))
+        coef = orc.clip_coef(sumsq, hp["max_grad_norm"])
+        assert coef < 1.0 and st.last_coef == coef, (st.last_coef, coef)
+
+        def job(lo):
+            k = min(CHUNK, n - lo)
+            pc, mc, vc = p[lo:lo + k], m[lo:lo + k], v[lo:lo + k]   # views: updated in place
+            return lo, orc.adamw(np.ascontiguousarray(gh[lo:lo + k]), orc.F16, pc, mc, vc, scale,
+                                 coef, step + 1, hpo, orc.F16)
+
+        with ThreadPoolExecutor(THREADS) as ex:
+            lps = dict(ex.map(job, range(0, n, CHUNK)))
+        got_p, got_m, got_v, got_lp = (to_host(t) for t in (opt.master, opt.exp_avg,
+                                                             opt.exp_avg_sq, ag))
+        for lo, lp in lps.items():
+            k = lp.size
+            w = "step %d, chunk at %d" % (step, lo)
+            assert_bitwise(got_p[lo:lo + k], p[lo:lo + k], "master, " + w)
+            assert_bitwise(got_m[lo:lo + k], m[lo:lo + k], "exp_avg, " + w)
+            assert_bitwise(got_v[lo:lo + k], v[lo:lo + k], "exp_avg_sq, " + w)
+            assert_bitwise(got_lp[lo:lo + k], lp, "slot, " + w)
+    del opt, base, master, ag, g
+    torch.cuda.empty_cache()
