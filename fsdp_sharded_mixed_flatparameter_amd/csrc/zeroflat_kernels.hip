@@ -65,8 +65,8 @@ constexpr int kMaxGridReduce = ZERO_MAX_PARTIALS;
 // launch of a few hundred thousand blocks streams a little slower than the
 // same tiles issued as consecutive launches of kSliceBlocks blocks (tile
 // ranges [t0, t1), same stream): on the 1.25e9-element update 6.24-6.38 ms
-// as one launch against 5.90-5.96 ms in slices of 16,384 blocks, and the
-// 8-slice reduce and the INT8 gather gained 4-6% the same way.  A kernel
+// as one launch against 5.86-5.96 ms in slices of 16,384 or 32,768 blocks,
+// and the 8-slice reduce and the INT8 gather gained 3-6% the same way.  A kernel
 // boundary makes every XCD finish before the next range starts, which keeps
 // the addresses in flight in one window; within one long launch the
 // dispatch order alone does not.  kLdsTwoBlocks is a dynamic LDS reservation
