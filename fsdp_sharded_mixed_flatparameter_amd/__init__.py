@@ -51,7 +51,7 @@ class zero_step_state_t(C.Structure):
                 ("beta1_pow", C.c_double), ("beta2_pow", C.c_double),
                 ("last_norm", C.c_double), ("last_coef", C.c_float),
                 ("last_skipped", C.c_int32), ("n_partials", C.c_int32),
-                ("reserved", C.c_int32), ("partials", C.c_double * ZERO_MAX_PARTIALS)]
+                ("tile_counter", C.c_int32), ("partials", C.c_double * ZERO_MAX_PARTIALS)]
 
 
 class zero_adamw_hparams_t(C.Structure):

@@ -81,6 +81,8 @@ constexpr int kMaxGridReduce = ZERO_MAX_PARTIALS;
 constexpr int64_t kSliceBlocks = 32768;
 constexpr unsigned kLdsTwoBlocks = 56 * 1024;
 constexpr int64_t kTwoBlocksMin = 8192;
+// the counter-scheduled update (adamw_sched_kernel) from this many tile groups
+constexpr int64_t kSchedMinGroups = 8192;
 
 // Native vectors for the non-temporal (streaming, read-once / write-once)
 // accesses: every array of the step is touched exactly once per launch.
@@ -1049,6 +1051,47 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamLaunch a, int64_t t
     }
 }
 
+// The update of a large shard without the INT8 epilogue: a persistent grid of
+// two blocks per compute unit takes groups of kWaves consecutive tiles (one
+// per wave) from a counter in the state, in the order the blocks ask, so the
+// tiles in flight stay in one narrow window of every array however the XCDs
+// drift (measured 0.6-2.8% faster than launch slices of 32,768 blocks on
+// three allocations; at full occupancy 10% slower).  Each tile is updated
+// exactly once whichever block takes it, so the results do not depend on the
+// order.  A block takes its next group while it updates the current one;
+// every block's last request comes back past the end, so there are exactly
+// ngroups + gridDim.x requests, and the block whose request is the last one
+// returns the counter to zero for the next launch.  A skipped step takes no
+// group and leaves the counter at zero.
+template <int GT, int PT>
+__global__ void __launch_bounds__(kThreads) adamw_sched_kernel(AdamLaunch a) {
+    const StepScalars s = read_step(a.st, a.beta1, a.beta2, a.max_norm);
+    if (s.skip) return;
+    unsigned* counter = reinterpret_cast<unsigned*>(&a.st->tile_counter);
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t ntiles = (a.n + kTile - 1) / kTile;
+    const int64_t nfull = a.n / kTile;
+    const unsigned ngroups = (unsigned)((ntiles + kWaves - 1) / kWaves);
+    __shared__ unsigned s_group;
+    unsigned next = 0;
+    if (threadIdx.x == 0) s_group = atomicAdd(counter, 1u);
+    __syncthreads();
+    unsigned g = s_group;
+    __syncthreads();
+    while (g < ngroups) {
+        if (threadIdx.x == 0) next = atomicAdd(counter, 1u);
+        const int64_t t = (int64_t)g * kWaves + w;
+        if (t < nfull) adam_tile_full<GT, PT, false>(a, s, t * kTile, lane);
+        else if (t < ntiles) adam_tile_part<GT, PT, false>(a, s, t * kTile, lane);
+        if (threadIdx.x == 0) s_group = next;
+        __syncthreads();
+        g = s_group;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0 && g == ngroups + gridDim.x - 1) atomicExch(counter, 0u);
+}
+
 // Loss scaler and counters after the step (one thread).
 __global__ void finalize_kernel(zero_step_state_t* st, double beta1, double beta2,
                                 double max_norm) {
@@ -1364,6 +1407,26 @@ __global__ void __launch_bounds__(kThreads) dequant_flat_kernel(DequantLaunch a,
 }
 
 // ---------------------------------------------------------------- launch helpers
+// compute units of the current device, looked up once per device
+constexpr int kMaxCuDevices = 64;
+std::atomic<int> g_cu_count[kMaxCuDevices];
+
+int cu_count_for_current_device(int* out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxCuDevices) return (int)hipErrorInvalidDevice;
+    int n = g_cu_count[dev].load(std::memory_order_acquire);
+    if (n <= 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return (int)e;
+        if (n <= 0) return (int)hipErrorInvalidDevice;
+        g_cu_count[dev].store(n, std::memory_order_release);
+    }
+    *out = n;
+    return 0;
+}
+
 int grid_for_tiles(int64_t ntiles, int cap) {
     int64_t g = (ntiles + kWaves - 1) / kWaves;
     if (g > cap) g = cap;
@@ -1508,6 +1571,17 @@ int launch_reduce_q8_v(const ReduceLaunch& a, void* stream) {
 template <int GT, int PT, bool QUANT>
 int launch_adamw_q(const AdamLaunch& a, void* stream) {
     const int64_t ntiles = (a.n + kTile - 1) / kTile;
+    const int64_t ngroups = (ntiles + kWaves - 1) / kWaves;
+    if (!QUANT && a.vec && ngroups >= kSchedMinGroups) {
+        int cus = 0;
+        const int e = cu_count_for_current_device(&cus);
+        if (e) return e;
+        int64_t grid = 2 * (int64_t)cus;                // two blocks per compute unit
+        if (grid > ngroups) grid = ngroups;
+        hipLaunchKernelGGL((adamw_sched_kernel<GT, PT>), dim3((unsigned)grid), dim3(kThreads),
+                           kLdsTwoBlocks, (hipStream_t)stream, a);
+        return (int)hipGetLastError();
+    }
     const int64_t slice = kSliceBlocks * kWaves;   // tiles per launch
     for (int64_t t0 = 0; t0 < ntiles; t0 += slice) {
         const int64_t t1 = ntiles - t0 < slice ? ntiles : t0 + slice;

@@ -189,3 +189,61 @@ def test_adamw_over_several_launches(zf, vector):
             assert_bitwise(got_lp[lo:lo + k], lp, "slot, " + w)
     del opt, base, master, ag, g
     torch.cuda.empty_cache()
+
+
+def test_adamw_group_counter_across_calls(zf):
+    """The update of a large shard takes its tile groups from a counter in the
+    step state, which every launch must return to zero.  Two FlatParameter
+    units share one state (one global norm): two updates per step on the same
+    state, a skipped step (an inf in unit 0) between two applied ones.  Every
+    element of both units against the oracle at each step, the counter zero
+    after each, nothing written by the skipped step."""
+    dev = torch.device("cuda:0")
+    sizes = (40_000_003, 34_000_001)        # at least 8,192 groups of four 1,024-element tiles
+    hp = dict(lr=3e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.5)
+    hpo = orc.Hparams(**hp)
+    scale = 256.0
+    state = zf.StepState(scale, False)
+    units = []
+    for u, n in enumerate(sizes):
+        master = torch.empty(n, device=dev)
+        synth.fill_normal(master, synth.stream_key("ctr-p", u), 0, 0.02)
+        units.append(dict(n=n, master=master, m=torch.zeros_like(master),
+                          v=torch.zeros_like(master), ag=torch.zeros(n, dtype=torch.float16, device=dev),
+                          g=torch.empty(n, dtype=torch.float16, device=dev),
+                          p_ref=to_host(master).copy(), m_ref=np.zeros(n, np.float32),
+                          v_ref=np.zeros(n, np.float32)))
+    applied = 0
+    for step, skip in enumerate((False, True, False)):
+        say("group counter step", step, "skip" if skip else "")
+        for u, U in enumerate(units):
+            synth.fill_normal(U["g"], synth.stream_key("ctr-g", u, step), 0, 1e-3 * scale)
+        if skip:
+            units[0]["g"][12345] = float("inf")
+        before = [to_host(U["master"]).copy() for U in units] if skip else None
+        for U in units:
+            zf.zero_unscale_norm(U["g"], state)
+        for u, U in enumerate(units):
+            zf.zero_adamw_shard_step(U["g"], U["master"], U["m"], U["v"], U["ag"], 0, hp, state,
+                                     finalize=u == len(units) - 1)
+        st = state.read()
+        assert st.tile_counter == 0
+        assert st.last_skipped == int(skip)
+        if skip:
+            for U, b in zip(units, before):
+                assert_bitwise(to_host(U["master"]), b, "master after a skipped step")
+            continue
+        applied += 1
+        gh = [to_host(U["g"]).copy() for U in units]
+        sumsq = sum(orc.unscale_stats(g, orc.F16, scale)[0] for g in gh)
+        coef = orc.clip_coef(sumsq, hp["max_grad_norm"])
+        assert coef < 1.0 and st.last_coef == coef
+        for U, g in zip(units, gh):
+            lp = orc.adamw(g, orc.F16, U["p_ref"], U["m_ref"], U["v_ref"], scale, coef, applied,
+                           hpo, orc.F16)
+            assert_bitwise(to_host(U["master"]), U["p_ref"], "master, step %d" % step)
+            assert_bitwise(to_host(U["m"]), U["m_ref"], "exp_avg, step %d" % step)
+            assert_bitwise(to_host(U["v"]), U["v_ref"], "exp_avg_sq, step %d" % step)
+            assert_bitwise(to_host(U["ag"]), lp, "slot, step %d" % step)
+    del units
+    torch.cuda.empty_cache()
