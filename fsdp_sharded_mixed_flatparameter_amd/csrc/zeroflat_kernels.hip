@@ -7,6 +7,8 @@
 //                    pass of a pre-reduced shard
 //   fold_kernel      the statistics' per-block partial sums, in a fixed order
 //   adamw_kernel     skip/clip prologue, fused AdamW, 16-bit write-back, INT8
+//   adamw_sched_kernel  the same (no INT8) for large shards: a persistent
+//                    grid taking groups of tiles from a counter in the state
 //   finalize_kernel  loss scaler and counters
 //   quant_kernel     INT8 of an existing 16-bit slot (quad tiles)
 //   quant8_kernel    the same on 16-byte aligned slots, eight elements per lane
@@ -28,8 +30,9 @@
 // elements is exactly one INT8 block, reduced across the wave.  All kU
 // slices' loads are issued before any arithmetic (bytes in flight per lane),
 // and every stream uses non-temporal loads/stores: each byte is touched once.
-// By default the AdamW grid holds one tile per wave and the hardware
-// dispatcher balances blocks as they retire.
+// The AdamW grid holds one tile per wave, issued in launch slices over tile
+// ranges; a large shard without the INT8 epilogue takes its tiles from a
+// counter instead (adamw_sched_kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1438,7 +1441,9 @@ int grid_for_tiles(int64_t ntiles, int cap) {
 // hardware dispatcher issues the blocks in order, so the tiles in flight at
 // any moment form one narrow window of each buffer.  (A persistent grid whose
 // waves walk the shard measured 5-10% slower: its waves drift apart and the
-// reads in flight spread over the buffers.)  A reduce of 16-bit or fp32
+// reads in flight spread over the buffers.  Tiles taken from a counter, as the
+// update does, would make each block's partial sum depend on which tiles it
+// took, and the norm on the run.)  A reduce of 16-bit or fp32
 // inputs takes one tile per wave (R = 1): on 8 fp16 slices of 1.25e9 elements
 // that measured 7-10% faster than runs of 16 tiles, whose waves work in as
 // many separate windows.  It is issued as launches of at most kSliceBlocks
