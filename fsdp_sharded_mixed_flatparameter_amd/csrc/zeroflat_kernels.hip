@@ -1522,21 +1522,46 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     const int N = a.n_ranks;
     const int pow2 = (N & (N - 1)) == 0;
     const float inv_n = 1.0f / (float)N;  // exact when N is a power of two
-    // reads in flight per lane: TU chunks x KC buffers (KC divides N).  Many
-    // 16-bit or fp32 buffers read one chunk of 16 buffers per step (7% faster
-    // than two chunks of 8 at 64 buffers); eight 16-bit buffers read four
-    // chunks of all eight (a whole tile in one step, 4-8% faster than two
-    // chunks); INT8 payloads keep two chunks of 8.
+    // reads in flight per lane: TU chunks x KC buffers (KC divides N), and with
+    // several buffer groups the next step's reads on top (the pipeline); a
+    // wave takes one tile.  Measured with the statistics on 16-bit buffers
+    // (TB/s, the kept shape first):
+    //   64 buffers: 1 x 16 5.93, 2 x 16 5.67, 4 x 16 5.82 (1 x 16 was also 7%
+    //               faster than 2 x 8 with runs of tiles)
+    //   32: 2 x 16 6.07 against 1 x 16 5.73;  16: 2 x 16 6.01 against 1 x 16
+    //   4.82 (one step: one chunk left too few reads in flight)
+    //   8: 4 x 8 (a whole tile in one step) 4-8% faster than 2 x 8
+    //   12: 4 x 4 6.15 against 2 x 4 5.81;  4: 2 x 4 6.18, 8 x 4 6.09, 4 x 4 5.45
+    //   2 and 6: 4 x 2 6.25 / 6.10, 8 x 2 6.06 / 5.99
+    //   odd (3): 4 x 1 6.22 against 8 x 1 5.87;  16 chunks per tile spill registers
+    // fp32 buffers (two registers per value more) keep the narrower shapes;
+    // INT8 payloads keep two chunks of 8.
     constexpr bool k16 = DT == ZERO_F16 || DT == ZERO_BF16;
-    if (DT != kQ8 && N % 16 == 0)
-        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 1, 16, ACC>(a, stream, inv_n, pow2);
-    else if (k16 && N == 8)
-        launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, (k16 ? 4 : 2), 8, ACC, true>(a, stream, inv_n, pow2);
-    else if (N % 8 == 0) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
-    else if (N % 4 == 0) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
-    else if (N % 2 == 0) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
-    else if (N == 1) launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 1, ACC>(a, stream, inv_n, pow2);
-    else launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 8, 1, ACC>(a, stream, inv_n, pow2);
+    constexpr int kTu16 = k16 ? 2 : 1;   // 16 or 32 16-bit buffers
+    constexpr int kTu4 = k16 ? 4 : 2;    // 12, 20, 28, ... 16-bit buffers
+    constexpr int kTuOdd = k16 ? 4 : 8;
+    if (DT != kQ8 && N % 16 == 0) {
+        if (k16 && N <= 32)
+            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu16, 16, ACC>(a, stream, inv_n, pow2);
+        else
+            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 1, 16, ACC>(a, stream, inv_n, pow2);
+    } else if (k16 && N == 8) {
+        launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, (k16 ? 4 : 2), 8, ACC, true>(a, stream, inv_n,
+                                                                                   pow2);
+    } else if (N % 8 == 0) {
+        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
+    } else if (N % 4 == 0) {
+        if (k16 && N > 4)
+            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu4, 4, ACC>(a, stream, inv_n, pow2);
+        else
+            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
+    } else if (N % 2 == 0) {
+        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
+    } else if (N == 1) {
+        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 1, ACC>(a, stream, inv_n, pow2);
+    } else {
+        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTuOdd, 1, ACC>(a, stream, inv_n, pow2);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (STATS) {
