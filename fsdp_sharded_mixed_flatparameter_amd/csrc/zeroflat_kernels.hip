@@ -1534,12 +1534,16 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     //   12: 4 x 4 6.15 against 2 x 4 5.81;  4: 2 x 4 6.18, 8 x 4 6.09, 4 x 4 5.45
     //   2 and 6: 4 x 2 6.25 / 6.10, 8 x 2 6.06 / 5.99
     //   odd (3): 4 x 1 6.22 against 8 x 1 5.87;  16 chunks per tile spill registers
-    // fp32 buffers (two registers per value more) keep the narrower shapes;
-    // INT8 payloads keep two chunks of 8.
+    //   24 and 40 (several groups of 8): 1 x 8 5.79 / 6.04 against 2 x 8 5.70 / 5.84
+    // fp32 buffers (two registers per value more): 2 x 8 for eight (6.08 against
+    // 5.92 with 4 x 8), 4 x 4 for four (6.32 against 5.89 with 2 x 4), 4 x 1 for
+    // three (6.08 against 5.62 with 8 x 1).  INT8 payloads: 2 x 8 (eight: 5.88
+    // against 5.60 with 4 x 8 and 5.45 with 1 x 8; 64: within 2% of 4 x 8).
     constexpr bool k16 = DT == ZERO_F16 || DT == ZERO_BF16;
     constexpr int kTu16 = k16 ? 2 : 1;   // 16 or 32 16-bit buffers
-    constexpr int kTu4 = k16 ? 4 : 2;    // 12, 20, 28, ... 16-bit buffers
-    constexpr int kTuOdd = k16 ? 4 : 8;
+    constexpr int kTu8 = k16 ? 1 : 2;    // 24, 40, 56, ... 16-bit buffers
+    constexpr int kTu4 = k16 || DT == ZERO_F32 ? 4 : 2;
+    constexpr int kTuOdd = DT == kQ8 ? 8 : 4;
     if (DT != kQ8 && N % 16 == 0) {
         if (k16 && N <= 32)
             launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu16, 16, ACC>(a, stream, inv_n, pow2);
@@ -1549,9 +1553,12 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
         launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, (k16 ? 4 : 2), 8, ACC, true>(a, stream, inv_n,
                                                                                    pow2);
     } else if (N % 8 == 0) {
-        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
+        if (k16)
+            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu8, 8, ACC>(a, stream, inv_n, pow2);
+        else
+            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
     } else if (N % 4 == 0) {
-        if (k16 && N > 4)
+        if (k16 ? N > 4 : (DT == ZERO_F32 && N == 4))
             launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu4, 4, ACC>(a, stream, inv_n, pow2);
         else
             launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
