@@ -332,6 +332,10 @@ constexpr int kQ8 = 3;
 constexpr int kPartFirst = 1;   // does the head elements (the shard's first launch)
 constexpr int kPartLast = 2;    // does the ragged tail (its last launch)
 constexpr int kPartAdd = 4;     // adds onto the partials of the launch before
+constexpr int kPartFold = 8;    // one launch of at most kFoldThreads blocks: its last
+                                // block folds the partials (no fold kernel)
+constexpr int kFoldThreads = 1024;   // fold_kernel's block (one partial per thread and pass)
+constexpr int kFoldU = 8;            // fold_kernel's loads in flight per thread
 
 __device__ __forceinline__ int64_t block_of(const ReduceLaunch& a, int64_t i) {
     return a.block_shift >= 0 ? (i >> a.block_shift) : i / a.block;
@@ -780,6 +784,42 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
             }
         }
         if (__ballot(ovf) != 0ull && lane == 0) atomicOr(&a.st->overflow, 1);
+        if (part & kPartFold) {
+            // A small reduce folds its own partials: each block counts itself
+            // in after its partial (device-scope release), and the block that
+            // counts last (acquire) adds them in fold_kernel's order -- virtual
+            // thread t of 1024 holds partial t (or +0), each virtual wave's
+            // butterfly, then the 16 wave sums in order -- so st->sumsq gets the
+            // same bits as from the fold kernel.  The count lives in the state's
+            // counter field and is returned to zero here.
+            __shared__ int s_last;
+            __shared__ double s_wave[kFoldThreads / 64];
+            unsigned* count = reinterpret_cast<unsigned*>(&a.st->tile_counter);
+            if (threadIdx.x == 0) {
+                __threadfence();
+                s_last = atomicAdd(count, 1u) == gridDim.x - 1;
+            }
+            __syncthreads();
+            if (s_last) {
+                __threadfence();
+                const int np = (int)gridDim.x;
+                for (int vw = (int)(threadIdx.x >> 6); vw < kFoldThreads / 64; vw += kWaves) {
+                    const int i = vw * 64 + lane;
+                    double x = 0.0;
+                    if (i < np) x = x + a.partials[i];
+                    x = wave_sum(x);
+                    if (lane == 0) s_wave[vw] = x;
+                }
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    double t = 0.0;
+#pragma unroll
+                    for (int w = 0; w < kFoldThreads / 64; ++w) t += s_wave[w];
+                    a.st->sumsq = a.st->sumsq + t;
+                    atomicExch(count, 0u);
+                }
+            }
+        }
     }
 }
 
@@ -790,8 +830,6 @@ __global__ void __launch_bounds__(kThreads) reduce_kernel(ReduceLaunch a, float 
 // in that order, with kFoldU loads in flight (an out-of-range slot adds +0,
 // which leaves a sum of non-negative terms unchanged); then the waves'
 // butterflies and the waves in index order.
-constexpr int kFoldThreads = 1024;
-constexpr int kFoldU = 8;
 __global__ void __launch_bounds__(kFoldThreads) fold_kernel(zero_step_state_t* st,
                                                             const double* partials) {
     const int n = st->n_partials;
@@ -1459,7 +1497,7 @@ constexpr int64_t kFillBlocks = 4096;
 constexpr int64_t kMaxLaunches = 64;
 constexpr int64_t kMaxGridPlain = int64_t(1) << 30;   // no partial sums to hold
 template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, int TU, int KC, bool ACC, bool G1>
-void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
+bool launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
     constexpr int64_t kT = 256 * TU;
     const int64_t hs = SHIFT ? a.head : 0;           // as the kernel splits the shard
     const int64_t nbody = a.n > hs ? a.n - hs : 0;
@@ -1491,6 +1529,7 @@ void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int po
     const int64_t chunk = cap * per_block;           // full tiles per launch
     int64_t t0 = 0;
     int part = kPartFirst;
+    bool folded = false;
     for (;;) {
         const int64_t t1 = nfull - t0 > chunk ? t0 + chunk : nfull;
         const bool last = t1 == nfull;
@@ -1501,6 +1540,11 @@ void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int po
             if (grid < tail) grid = tail;
         }
         if (grid < 1) grid = 1;
+        // a reduce of one small launch folds its own partial sums
+        if (STATS && part == kPartFirst && last && grid <= kFoldThreads) {
+            part |= kPartFold;
+            folded = true;
+        }
         const unsigned lds = two && grid >= kTwoBlocksMin ? kLdsTwoBlocks : 0u;
         hipLaunchKernelGGL((reduce_kernel<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, G1>),
                            dim3((unsigned)grid), dim3(kThreads), lds, (hipStream_t)stream, a, inv_n,
@@ -1509,12 +1553,14 @@ void launch_reduce_grid(const ReduceLaunch& a, void* stream, float inv_n, int po
         t0 = t1;
         part = kPartAdd;
     }
+    return folded;
 }
 
 template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, int TU, int KC, bool ACC>
-void launch_reduce_shape(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
-    if (a.n_ranks == KC) launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, true>(a, stream, inv_n, pow2);
-    else launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, false>(a, stream, inv_n, pow2);
+bool launch_reduce_shape(const ReduceLaunch& a, void* stream, float inv_n, int pow2) {
+    if (a.n_ranks == KC)
+        return launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, true>(a, stream, inv_n, pow2);
+    return launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, TU, KC, ACC, false>(a, stream, inv_n, pow2);
 }
 
 template <int DT, bool VEC, bool SHIFT, bool WRITE, bool STATS, bool ACC>
@@ -1544,34 +1590,35 @@ int launch_reduce_t(const ReduceLaunch& a, void* stream) {
     constexpr int kTu8 = k16 ? 1 : 2;    // 24, 40, 56, ... 16-bit buffers
     constexpr int kTu4 = k16 || DT == ZERO_F32 ? 4 : 2;
     constexpr int kTuOdd = DT == kQ8 ? 8 : 4;
+    bool folded = false;
     if (DT != kQ8 && N % 16 == 0) {
         if (k16 && N <= 32)
-            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu16, 16, ACC>(a, stream, inv_n, pow2);
+            folded = launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu16, 16, ACC>(a, stream, inv_n, pow2);
         else
-            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 1, 16, ACC>(a, stream, inv_n, pow2);
+            folded = launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 1, 16, ACC>(a, stream, inv_n, pow2);
     } else if (k16 && N == 8) {
-        launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, (k16 ? 4 : 2), 8, ACC, true>(a, stream, inv_n,
-                                                                                   pow2);
+        folded = launch_reduce_grid<DT, VEC, SHIFT, WRITE, STATS, (k16 ? 4 : 2), 8, ACC, true>(
+            a, stream, inv_n, pow2);
     } else if (N % 8 == 0) {
         if (k16)
-            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu8, 8, ACC>(a, stream, inv_n, pow2);
+            folded = launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu8, 8, ACC>(a, stream, inv_n, pow2);
         else
-            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
+            folded = launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 8, ACC>(a, stream, inv_n, pow2);
     } else if (N % 4 == 0) {
         if (k16 ? N > 4 : (DT == ZERO_F32 && N == 4))
-            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu4, 4, ACC>(a, stream, inv_n, pow2);
+            folded = launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTu4, 4, ACC>(a, stream, inv_n, pow2);
         else
-            launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
+            folded = launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 4, ACC>(a, stream, inv_n, pow2);
     } else if (N % 2 == 0) {
-        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
+        folded = launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 4, 2, ACC>(a, stream, inv_n, pow2);
     } else if (N == 1) {
-        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 1, ACC>(a, stream, inv_n, pow2);
+        folded = launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, 2, 1, ACC>(a, stream, inv_n, pow2);
     } else {
-        launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTuOdd, 1, ACC>(a, stream, inv_n, pow2);
+        folded = launch_reduce_shape<DT, VEC, SHIFT, WRITE, STATS, kTuOdd, 1, ACC>(a, stream, inv_n, pow2);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
-    if (STATS) {
+    if (STATS && !folded) {
         hipLaunchKernelGGL(fold_kernel, dim3(1), dim3(kFoldThreads), 0, (hipStream_t)stream, a.st,
                            a.partials);
         e = hipGetLastError();

@@ -167,9 +167,11 @@ typedef struct {
     int32_t last_skipped;    /* 1 if the step was skipped (overflow) */
     /* internal: per-block partial sums of the last statistics launch */
     int32_t n_partials;
-    /* internal: the update's tile-group counter.  Zero between launches: the
-     * init sets it, and every launch of the update that uses it returns it to
-     * zero before it ends; a state is not shared by overlapping launches. */
+    /* internal: a counter for one launch at a time -- the update's tile-group
+     * counter, or a small reduce's count of finished blocks (its last block
+     * folds the partials).  Zero between launches: the init sets it, and every
+     * launch that uses it returns it to zero before it ends; a state is not
+     * shared by overlapping launches. */
     int32_t tile_counter;
     double partials[ZERO_MAX_PARTIALS];
 } zero_step_state_t;
