@@ -8,18 +8,21 @@ fp32 master/m/v shard and writes the fp16 parameters into the rank's slot of a
 full 20 GB All-Gather buffer.  Inputs are synthetic (seeded, generated on the
 GPU before timing) and resident in HBM when the timed region starts.
 
-A "step" is the whole path: statistics kernel + fold, the AdamW kernel, and
-the loss-scaler finalize.  The AdamW kernel is the dominant one; its duration
-is taken with HIP events on the launch stream around every launch.  Where the
+A "step" is the whole path: statistics kernel + fold, the AdamW update, and
+the loss-scaler finalize.  The AdamW update is the dominant kernel (for this
+shard one launch of the counter-scheduled kernel); its duration is taken with
+HIP events on the launch stream around every call.  Where the
 step's arrays land in physical memory moves every streaming kernel on them,
 so the arrays are allocated afresh three times, each allocation running the
 warm-up and the timed steps; `value` and `roofline` cover all of them and
 `allocations` lists each with the median and minimum.  The same process
 measures the practical ceilings: read-only, write-only and copy streams over
-4 GiB, and on the step's own arrays the update's byte mix and a plain copy;
-`roofline` gives the AdamW rate against 8 TB/s, against each of these, and
-against the read-only and write-only rates taken back to back for its 14 B
-read and 14 B written per parameter.
+4 GiB, and on the step's own arrays the update's byte mix and a plain copy,
+each in three launch forms (one launch, launch slices, slices with two blocks
+per compute unit) with the fastest kept; `roofline` gives the AdamW rate
+against 8 TB/s, against each of these, and against the fastest read-only and
+write-only rates taken back to back for its 14 B read and 14 B written per
+parameter.
 
 Also timed, each as whole steps: the other workloads (8- and 64-way reduces,
 the 70B INT8 shard, the 7B block, the Tiny MLP, gradient accumulation over 2
