@@ -674,7 +674,7 @@ def _best_form(torch, fn, reps):
 
 
 def run_ceilings(torch, nbytes=4 << 30, reps=5):
-    """The practical HBM ceilings of this box, measured in the same process as
+    """The practical HBM ceilings of this machine, measured in the same process as
     the step with the streaming calibration kernels of synth (non-temporal
     16-byte accesses, HIP events on the launch stream): read-only, write-only
     and copy, each in every launch form, the fastest kept (the one-launch
