@@ -96,6 +96,7 @@ def test_state_struct_size_and_init(zf):
     assert (st.loss_scale, st.min_scale, st.dynamic, st.window) == (1024.0, 2.0, 1, 7)
     assert (st.step, st.good_steps, st.sumsq, st.overflow) == (0, 0, 0.0, 0)
     assert st.beta1_pow == 1.0 and st.beta2_pow == 1.0
+    assert st.n_partials == 0 and st.tile_counter == 0   # the launch counter starts at zero
 
 
 @pytest.mark.parametrize("scale,dyn,window,floor", [
