@@ -26,7 +26,9 @@ parameter.
 
 Also timed, each as whole steps: the other workloads (8- and 64-way reduces,
 the 70B INT8 shard, the 7B block, the Tiny MLP, gradient accumulation over 2
-micro-steps, INT8-quantised rank gradients), the ZeRO-Offload step (the
+micro-steps, INT8-quantised rank gradients; for the 16-bit reduces also the
+reduce call alone, against its bytes at the read-only and write-only ceilings
+back to back), the ZeRO-Offload step (the
 update on host cores), and the INT8 All-Gather consumer (gathered slots
 dequantised into the full flat parameter) on the 7B block and the whole 70B
 flat parameter.  The oracle is timed on one host core beside the headline and
@@ -453,6 +455,22 @@ def run_workload(zf, torch, w, steps, warmup, flush=False, shift=0):
         del scratch
     st = opt.state.read()
     assert st.last_skipped == 0, "unexpected skipped step"
+    reduce_call = None
+    if w.reduce and not w.grad_int8 and w.micro_steps <= 1 and not flush:
+        # the reduce with its statistics alone (its launches and the fold),
+        # timed by HIP events on the stream it runs on, into the optimizer's
+        # reduce buffer with a state of its own
+        red, st2 = opt.reduced_buffer(), zf.StepState(w.loss_scale, False)
+        rms = _event_ms_back_to_back(
+            torch, lambda: zf.zero_grad_reduce_shard(grads, shift, S, w.op, red, st2),
+            max(10, steps))
+        nbytes = (w.n_ranks * grads[0].element_size() + 4) * S
+        reduce_call = {"ms": rms, "bytes": nbytes,
+                       "read_bytes": w.n_ranks * grads[0].element_size() * S,
+                       "write_bytes": 4 * S, "GBps": nbytes / (rms * 1e-3) / 1e9,
+                       "what": "zero_grad_reduce_shard with statistics alone (reduce_kernel "
+                               "launches + fold), median of HIP-event-timed calls issued back to back"}
+        del red, st2
     del opt, grads, ag, master, q, qs
     torch.cuda.empty_cache()
     bpp = step_bytes_per_param(w)
@@ -464,7 +482,22 @@ def run_workload(zf, torch, w, steps, warmup, flush=False, shift=0):
     res.update({"ms_per_step": ms, "params_per_s": S / (ms * 1e-3), "bytes_per_param": bpp,
                 "step_GBps": bpp * S / (ms * 1e-3) / 1e9,
                 "step_frac_of_peak": bpp * S / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+    if reduce_call:
+        res["reduce_call"] = reduce_call
     return res
+
+
+def add_reduce_bounds(variants, ceilings):
+    """Each timed reduce against its bytes read and written at the same
+    process's read-only and write-only ceilings, back to back."""
+    for r in variants.values():
+        rc = r.get("reduce_call")
+        if not rc:
+            continue
+        t = (rc["read_bytes"] / (ceilings["read"]["GBps"] * 1e9) +
+             rc["write_bytes"] / (ceilings["write"]["GBps"] * 1e9)) * 1e3
+        rc["additive_read_write_ms"] = t
+        rc["frac_of_additive_read_write"] = t / rc["ms"]
 
 
 def run_graph(zf, torch, w, steps, warmup):
@@ -663,6 +696,24 @@ LAUNCH_FORMS = (("one_launch", 0, 0), ("slices", SLICE_BLOCKS, 0),
                 ("slices_two_blocks_per_cu", SLICE_BLOCKS, LDS_TWO_BLOCKS))
 
 
+def _event_ms_back_to_back(torch, fn, reps):
+    """Median ms of fn by HIP events around each call, the calls issued back
+    to back (no host wait between them, so the launches' host time stays off
+    the device's timeline); the first call is a warm-up."""
+    fn()
+    evs = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return ms[len(ms) // 2]
+
+
 def _best_form(torch, fn, reps):
     """ms of fn in each launch form; (best ms, {form: ms})."""
     from synth import synth
@@ -749,6 +800,8 @@ def main():
             if base in out["variants"]:
                 r["vs_aligned"] = out["variants"][base]["ms_per_step"] / r["ms_per_step"]
             out["variants"][name] = r
+        if "ceilings" in out:
+            add_reduce_bounds(out["variants"], out["ceilings"])
         if sel("tiny_mlp_n4_graph"):
             out["variants"]["tiny_mlp_n4_graph"] = run_graph(
                 zf, torch, WORKLOADS["tiny_mlp_n4"], max(20, args.steps), 5)
@@ -831,7 +884,9 @@ def run_headline(zf, torch, w, args):
                                 "are over all of them" % (N_ALLOC, args.steps)},
         "step_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"bound": "hbm", "kernel": "adamw_kernel (fused AdamW + fp16 write-back)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "adamw_sched_kernel<1, 1> (fused AdamW + fp16 write-back, one "
+                               "counter-scheduled launch)",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": read_traffic(),
                      "algorithmic_bytes_per_launch": adam_bytes,
