@@ -470,6 +470,17 @@ def run_workload(zf, torch, w, steps, warmup, flush=False, shift=0):
                        "write_bytes": 4 * S, "GBps": nbytes / (rms * 1e-3) / 1e9,
                        "what": "zero_grad_reduce_shard with statistics alone (reduce_kernel "
                                "launches + fold), median of HIP-event-timed calls issued back to back"}
+        if shift == 0:
+            # the same N buffers read at once by a read-only calibration kernel
+            # (N concurrent streams, the fastest launch form)
+            sink = torch.zeros(1, dtype=torch.int32, device=dev)
+            rbytes = grads[0].element_size() * S
+            best, forms = _best_form(torch, lambda: synth.read_streams(grads, rbytes, sink),
+                                     max(5, steps))
+            reduce_call["read_same_buffers_GBps"] = w.n_ranks * rbytes / (best * 1e-3) / 1e9
+            reduce_call["read_same_buffers_GBps_by_form"] = {
+                k: w.n_ranks * rbytes / (v * 1e-3) / 1e9 for k, v in forms.items()}
+            del sink
         del red, st2
     del opt, grads, ag, master, q, qs
     torch.cuda.empty_cache()
@@ -498,6 +509,12 @@ def add_reduce_bounds(variants, ceilings):
              rc["write_bytes"] / (ceilings["write"]["GBps"] * 1e9)) * 1e3
         rc["additive_read_write_ms"] = t
         rc["frac_of_additive_read_write"] = t / rc["ms"]
+        if "read_same_buffers_GBps" in rc:
+            # the same with the read side at the rate of these N buffers read at once
+            t2 = (rc["read_bytes"] / (rc["read_same_buffers_GBps"] * 1e9) +
+                  rc["write_bytes"] / (ceilings["write"]["GBps"] * 1e9)) * 1e3
+            rc["additive_same_buffers_ms"] = t2
+            rc["frac_of_additive_same_buffers"] = t2 / rc["ms"]
 
 
 def run_graph(zf, torch, w, steps, warmup):
@@ -673,29 +690,6 @@ def run_offload(zf, torch, w, steps, warmup):
                     % threads}
 
 
-def _event_ms(torch, fn, reps):
-    ms = []
-    for _ in range(reps + 1):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms.append(e0.elapsed_time(e1))
-    ms = sorted(ms[1:])
-    return ms[len(ms) // 2]
-
-
-# launch forms of the calibration streams: one launch, the library's launch
-# slices of 32,768 blocks, and those slices with two resident blocks per
-# compute unit (56 KiB of dynamic LDS reserved); a stream's ceiling is the
-# fastest form
-SLICE_BLOCKS, LDS_TWO_BLOCKS = 32768, 56 * 1024
-LAUNCH_FORMS = (("one_launch", 0, 0), ("slices", SLICE_BLOCKS, 0),
-                ("slices_two_blocks_per_cu", SLICE_BLOCKS, LDS_TWO_BLOCKS))
-
-
 def _event_ms_back_to_back(torch, fn, reps):
     """Median ms of fn by HIP events around each call, the calls issued back
     to back (no host wait between them, so the launches' host time stays off
@@ -714,13 +708,22 @@ def _event_ms_back_to_back(torch, fn, reps):
     return ms[len(ms) // 2]
 
 
+# launch forms of the calibration streams: one launch, the library's launch
+# slices of 32,768 blocks, and those slices with two resident blocks per
+# compute unit (56 KiB of dynamic LDS reserved); a stream's ceiling is the
+# fastest form
+SLICE_BLOCKS, LDS_TWO_BLOCKS = 32768, 56 * 1024
+LAUNCH_FORMS = (("one_launch", 0, 0), ("slices", SLICE_BLOCKS, 0),
+                ("slices_two_blocks_per_cu", SLICE_BLOCKS, LDS_TWO_BLOCKS))
+
+
 def _best_form(torch, fn, reps):
     """ms of fn in each launch form; (best ms, {form: ms})."""
     from synth import synth
     forms = {}
     for name, sl, lds in LAUNCH_FORMS:
         with synth.launch_form(sl, lds):
-            forms[name] = _event_ms(torch, fn, reps)
+            forms[name] = _event_ms_back_to_back(torch, fn, reps)
     return min(forms.values()), forms
 
 

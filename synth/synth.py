@@ -80,6 +80,9 @@ def _gpu_lib():
         L.synth_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
         L.synth_read.restype = C.c_int
         L.synth_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+        L.synth_read_streams.restype = C.c_int
+        L.synth_read_streams.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_void_p,
+                                         C.c_void_p]
         L.synth_write.restype = C.c_int
         L.synth_write.argtypes = [C.c_void_p, C.c_int64, C.c_uint32, C.c_void_p]
         L.synth_mix28.restype = C.c_int
@@ -208,6 +211,19 @@ def read_stream(src, sink, stream=None):
                                C.c_void_p(sink.data_ptr()), _stream(stream))
     if rc != 0:
         raise RuntimeError("synth_read failed: hip error %d" % rc)
+
+
+def read_streams(bufs, nbytes, sink, stream=None):
+    """Read the first `nbytes` of every tensor in `bufs` (at most 128, 8-byte
+    aligned) at once, as many concurrent streams (calibration); `sink` is a
+    1-element int32 tensor."""
+    ptrs = (C.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+    for b in bufs:
+        assert b.is_cuda and b.numel() * b.element_size() >= nbytes
+    rc = _gpu_lib().synth_read_streams(ptrs, len(bufs), nbytes, C.c_void_p(sink.data_ptr()),
+                                       _stream(stream))
+    if rc != 0:
+        raise RuntimeError("synth_read_streams failed: hip error %d" % rc)
 
 
 def write_stream(dst, val=0x3f800000, stream=None):

@@ -89,6 +89,7 @@ __global__ void __launch_bounds__(256) fill_codes(uint64_t key, int64_t start, i
  * them, with non-temporal accesses (every byte is touched once), and blocks
  * loop over spans when the grid is smaller than the copy. */
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __global__ void __launch_bounds__(256) copy16(const u32x4* __restrict__ src,
                                               u32x4* __restrict__ dst, int64_t n16) {
     for (int64_t b = (int64_t)blockIdx.x * 1024; b < n16; b += (int64_t)gridDim.x * 1024) {
@@ -125,6 +126,32 @@ __global__ void __launch_bounds__(256) read16(const u32x4* __restrict__ src, int
     if (x == never) sink[0] = x;
 }
 
+/* Read-only pass over up to kMaxStreams buffers of the same size at once: a
+ * block reads 256 consecutive 8-byte words of every buffer (one per thread),
+ * 16 buffers in flight; the sum is stored only if it equals `never`, which
+ * keeps the loads live. */
+constexpr int kMaxStreams = 128;
+struct StreamPtrs {
+    const u32x2* p[kMaxStreams];
+};
+template <int KC>
+__global__ void __launch_bounds__(256) read_streams8(StreamPtrs b, int nbuf, int64_t w0,
+                                                     int64_t nw, uint32_t never,
+                                                     uint32_t* __restrict__ sink) {
+    const int64_t i = w0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t x = 0;
+    if (i < nw) {
+        for (int k0 = 0; k0 < nbuf; k0 += KC) {
+            u32x2 v[KC];
+#pragma unroll
+            for (int kk = 0; kk < KC; ++kk) v[kk] = __builtin_nontemporal_load(b.p[k0 + kk] + i);
+#pragma unroll
+            for (int kk = 0; kk < KC; ++kk) x += v[kk].x ^ v[kk].y;
+        }
+    }
+    if (x == never) sink[0] = x;
+}
+
 /* Write-only stream of 16-byte words (non-temporal), 16 KiB per block and pass. */
 __global__ void __launch_bounds__(256) write16(u32x4* __restrict__ dst, int64_t n16, uint32_t val) {
     for (int64_t b = (int64_t)blockIdx.x * 1024; b < n16; b += (int64_t)gridDim.x * 1024) {
@@ -142,7 +169,6 @@ __global__ void __launch_bounds__(256) write16(u32x4* __restrict__ dst, int64_t 
  * per wave; in slice u lane l holds elements 256u + 4l .. 4l+3) with
  * non-temporal accesses.  ntiles full tiles, one per wave. */
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __global__ void __launch_bounds__(256) mix28(const uint16_t* __restrict__ g, float* __restrict__ p,
                                              float* __restrict__ m, float* __restrict__ v,
                                              uint16_t* __restrict__ lp, int64_t ntiles) {
@@ -275,6 +301,38 @@ int synth_read(const void* src, int64_t nbytes, void* sink, void* stream) {
         hipLaunchKernelGGL(read16, dim3((int)((nw + 1023) / 1024)), dim3(256), g_lds_bytes,
                            (hipStream_t)stream, (const u32x4*)src + w0, nw, 0x9e3779b9u,
                            (uint32_t*)sink);
+    }
+    return (int)hipGetLastError();
+}
+
+/* Read-only pass over nbuf buffers of nbytes each at once (bufs: a host
+ * array of device pointers; nbytes a multiple of 8, every buffer 8-byte
+ * aligned; 1 <= nbuf <= 128); sink: one writable uint32. */
+int synth_read_streams(const void* const* bufs, int32_t nbuf, int64_t nbytes, void* sink,
+                       void* stream) {
+    if (nbytes <= 0) return 0;
+    if (nbuf < 1 || nbuf > kMaxStreams || (nbytes & 7)) return (int)hipErrorInvalidValue;
+    StreamPtrs b;
+    for (int k = 0; k < kMaxStreams; ++k) b.p[k] = nullptr;
+    for (int k = 0; k < nbuf; ++k) {
+        if (!bufs[k] || ((uintptr_t)bufs[k] & 7)) return (int)hipErrorInvalidValue;
+        b.p[k] = (const u32x2*)bufs[k];
+    }
+    const int64_t nw = nbytes / 8;
+    const int64_t blocks = (nw + 255) / 256;
+    const int64_t per = spans_per_launch(blocks);
+    for (int64_t s0 = 0; s0 < blocks; s0 += per) {
+        const int64_t nb = blocks - s0 < per ? blocks - s0 : per;
+        const int64_t w0 = s0 * 256;
+        if (nbuf % 16 == 0)
+            hipLaunchKernelGGL(read_streams8<16>, dim3((unsigned)nb), dim3(256), g_lds_bytes,
+                               (hipStream_t)stream, b, nbuf, w0, nw, 0x9e3779b9u, (uint32_t*)sink);
+        else if (nbuf % 8 == 0)
+            hipLaunchKernelGGL(read_streams8<8>, dim3((unsigned)nb), dim3(256), g_lds_bytes,
+                               (hipStream_t)stream, b, nbuf, w0, nw, 0x9e3779b9u, (uint32_t*)sink);
+        else
+            hipLaunchKernelGGL(read_streams8<1>, dim3((unsigned)nb), dim3(256), g_lds_bytes,
+                               (hipStream_t)stream, b, nbuf, w0, nw, 0x9e3779b9u, (uint32_t*)sink);
     }
     return (int)hipGetLastError();
 }
