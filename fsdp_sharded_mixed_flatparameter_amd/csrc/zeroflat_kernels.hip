@@ -31,8 +31,8 @@
 // slices' loads are issued before any arithmetic (bytes in flight per lane),
 // and every stream uses non-temporal loads/stores: each byte is touched once.
 // The AdamW grid holds one tile per wave, issued in launch slices over tile
-// ranges; a large shard without the INT8 epilogue takes its tiles from a
-// counter instead (adamw_sched_kernel).
+// ranges; a large shard takes its tiles from a counter instead
+// (adamw_sched_kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1092,19 +1092,21 @@ __global__ void __launch_bounds__(kThreads) adamw_kernel(AdamLaunch a, int64_t t
     }
 }
 
-// The update of a large shard without the INT8 epilogue: a persistent grid of
-// two blocks per compute unit takes groups of kWaves consecutive tiles (one
-// per wave) from a counter in the state, in the order the blocks ask, so the
-// tiles in flight stay in one narrow window of every array however the XCDs
-// drift (measured 0.6-2.8% faster than launch slices of 32,768 blocks on
-// three allocations; at full occupancy 10% slower).  Each tile is updated
-// exactly once whichever block takes it, so the results do not depend on the
-// order.  A block takes its next group while it updates the current one;
-// every block's last request comes back past the end, so there are exactly
-// ngroups + gridDim.x requests, and the block whose request is the last one
-// returns the counter to zero for the next launch.  A skipped step takes no
-// group and leaves the counter at zero.
-template <int GT, int PT>
+// The update of a large shard (with or without the INT8 epilogue): a
+// persistent grid of two blocks per compute unit takes groups of kWaves
+// consecutive tiles (one per wave) from a counter in the state, in the order
+// the blocks ask, so the tiles in flight stay in one narrow window of every
+// array however the XCDs drift (measured 0.6-2.8% faster than launch slices
+// of 32,768 blocks on three allocations, at full occupancy 10% slower; with
+// the INT8 epilogue 4% faster than full-occupancy slices on three of four
+// allocations, 5% slower on the fourth, and within 1.3% across all four).
+// Each tile is updated exactly once whichever block takes it, so the results
+// do not depend on the order.  A block takes its next group while it updates
+// the current one; every block's last request comes back past the end, so
+// there are exactly ngroups + gridDim.x requests, and the block whose request
+// is the last one returns the counter to zero for the next launch.  A skipped
+// step takes no group and leaves the counter at zero.
+template <int GT, int PT, bool QUANT>
 __global__ void __launch_bounds__(kThreads) adamw_sched_kernel(AdamLaunch a) {
     const StepScalars s = read_step(a.st, a.beta1, a.beta2, a.max_norm);
     if (s.skip) return;
@@ -1123,8 +1125,8 @@ __global__ void __launch_bounds__(kThreads) adamw_sched_kernel(AdamLaunch a) {
     while (g < ngroups) {
         if (threadIdx.x == 0) next = atomicAdd(counter, 1u);
         const int64_t t = (int64_t)g * kWaves + w;
-        if (t < nfull) adam_tile_full<GT, PT, false>(a, s, t * kTile, lane);
-        else if (t < ntiles) adam_tile_part<GT, PT, false>(a, s, t * kTile, lane);
+        if (t < nfull) adam_tile_full<GT, PT, QUANT>(a, s, t * kTile, lane);
+        else if (t < ntiles) adam_tile_part<GT, PT, QUANT>(a, s, t * kTile, lane);
         if (threadIdx.x == 0) s_group = next;
         __syncthreads();
         g = s_group;
@@ -1656,14 +1658,14 @@ template <int GT, int PT, bool QUANT>
 int launch_adamw_q(const AdamLaunch& a, void* stream) {
     const int64_t ntiles = (a.n + kTile - 1) / kTile;
     const int64_t ngroups = (ntiles + kWaves - 1) / kWaves;
-    if (!QUANT && a.vec && ngroups >= kSchedMinGroups) {
+    if (a.vec && ngroups >= kSchedMinGroups) {
         int cus = 0;
         const int e = cu_count_for_current_device(&cus);
         if (e) return e;
         int64_t grid = 2 * (int64_t)cus;                // two blocks per compute unit
         if (grid > ngroups) grid = ngroups;
-        hipLaunchKernelGGL((adamw_sched_kernel<GT, PT>), dim3((unsigned)grid), dim3(kThreads),
-                           kLdsTwoBlocks, (hipStream_t)stream, a);
+        hipLaunchKernelGGL((adamw_sched_kernel<GT, PT, QUANT>), dim3((unsigned)grid),
+                           dim3(kThreads), kLdsTwoBlocks, (hipStream_t)stream, a);
         return (int)hipGetLastError();
     }
     const int64_t slice = kSliceBlocks * kWaves;   // tiles per launch

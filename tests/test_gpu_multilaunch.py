@@ -195,9 +195,10 @@ def test_adamw_group_counter_across_calls(zf):
     """The update of a large shard takes its tile groups from a counter in the
     step state, which every launch must return to zero.  Two FlatParameter
     units share one state (one global norm): two updates per step on the same
-    state, a skipped step (an inf in unit 0) between two applied ones.  Every
-    element of both units against the oracle at each step, the counter zero
-    after each, nothing written by the skipped step."""
+    state, a skipped step (an inf in unit 0) between two applied ones; unit 1
+    also writes the INT8 codes and block scales of its slot.  Every element of
+    both units (and unit 1's codes and scales) against the oracle at each
+    step, the counter zero after each, nothing written by the skipped step."""
     dev = torch.device("cuda:0")
     sizes = (40_000_003, 34_000_001)        # at least 8,192 groups of four 1,024-element tiles
     hp = dict(lr=3e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.5)
@@ -212,7 +213,9 @@ def test_adamw_group_counter_across_calls(zf):
                           v=torch.zeros_like(master), ag=torch.zeros(n, dtype=torch.float16, device=dev),
                           g=torch.empty(n, dtype=torch.float16, device=dev),
                           p_ref=to_host(master).copy(), m_ref=np.zeros(n, np.float32),
-                          v_ref=np.zeros(n, np.float32)))
+                          v_ref=np.zeros(n, np.float32),
+                          q=torch.zeros(n, dtype=torch.int8, device=dev) if u == 1 else None,
+                          qs=torch.zeros(-(-n // 256), device=dev) if u == 1 else None))
     applied = 0
     for step, skip in enumerate((False, True, False)):
         say("group counter step", step, "skip" if skip else "")
@@ -225,6 +228,7 @@ def test_adamw_group_counter_across_calls(zf):
             zf.zero_unscale_norm(U["g"], state)
         for u, U in enumerate(units):
             zf.zero_adamw_shard_step(U["g"], U["master"], U["m"], U["v"], U["ag"], 0, hp, state,
+                                     q_buf=U["q"], q_scales=U["qs"],
                                      finalize=u == len(units) - 1)
         st = state.read()
         assert st.tile_counter == 0
@@ -245,5 +249,9 @@ def test_adamw_group_counter_across_calls(zf):
             assert_bitwise(to_host(U["m"]), U["m_ref"], "exp_avg, step %d" % step)
             assert_bitwise(to_host(U["v"]), U["v_ref"], "exp_avg_sq, step %d" % step)
             assert_bitwise(to_host(U["ag"]), lp, "slot, step %d" % step)
+            if U["q"] is not None:
+                rq, rs = orc.quant_int8(lp, orc.F16, 256)
+                assert_bitwise(to_host(U["q"]), rq, "INT8 codes, step %d" % step)
+                assert_bitwise(to_host(U["qs"]), rs, "INT8 scales, step %d" % step)
     del units
     torch.cuda.empty_cache()
