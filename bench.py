@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the other workloads")
+    ap.add_argument("--no-reduce-call", action="store_true",
+                    help="skip timing the 16-bit reduces alone (keeps a profiled run's launches "
+                         "to the steps)")
     ap.add_argument("--only", default="",
                     help="comma-separated workloads to run alone (10b_n8 for the headline, a "
                          "variant, 10b_n8_reduce8_shift1, tiny_mlp_n4_graph, offload or a "
@@ -356,7 +359,7 @@ def step_bytes_per_param(w):
 FLUSHED = ("tiny_mlp_n4", "llama7b_block_n8")   # working sets within a few times the 256 MB cache
 
 
-def run_workload(zf, torch, w, steps, warmup, flush=False, shift=0):
+def run_workload(zf, torch, w, steps, warmup, flush=False, shift=0, time_reduce=True):
     """Whole steps of any workload (inputs generated on the GPU first).  With
     `flush`, a 512 MB scratch buffer is streamed before each timed step, so the
     step starts with none of its data in the 256 MB Infinity Cache, and each
@@ -456,7 +459,7 @@ def run_workload(zf, torch, w, steps, warmup, flush=False, shift=0):
     st = opt.state.read()
     assert st.last_skipped == 0, "unexpected skipped step"
     reduce_call = None
-    if w.reduce and not w.grad_int8 and w.micro_steps <= 1 and not flush:
+    if time_reduce and w.reduce and not w.grad_int8 and w.micro_steps <= 1 and not flush:
         # the reduce with its statistics alone (its launches and the fold),
         # timed by HIP events on the stream it runs on, into the optimizer's
         # reduce buffer with a state of its own
@@ -784,7 +787,7 @@ def main():
             if not sel(name):
                 continue
             r = run_workload(zf, torch, WORKLOADS[name], max(3, args.steps // 2), 2,
-                             flush=name in FLUSHED)
+                             flush=name in FLUSHED, time_reduce=not args.no_reduce_call)
             r["what"] = what
             if not args.no_cpu_baseline:
                 r["cpu_baseline"] = cpu_baseline_workload(torch, WORKLOADS[name],
@@ -796,7 +799,8 @@ def main():
         for name, base in (("10b_n8_reduce8_shift1", "10b_n8_reduce8"),):
             if not sel(name):
                 continue
-            r = run_workload(zf, torch, WORKLOADS[base], max(3, args.steps // 2), 2, shift=1)
+            r = run_workload(zf, torch, WORKLOADS[base], max(3, args.steps // 2), 2, shift=1,
+                             time_reduce=not args.no_reduce_call)
             r["what"] = ("as %s, with every rank slice starting 1 element into its buffer and "
                          "the slot 1 element past its place: the reduce's shifted vector path "
                          "and the update's joined slot words" % base)
