@@ -7,8 +7,8 @@
 //                    pass of a pre-reduced shard
 //   fold_kernel      the statistics' per-block partial sums, in a fixed order
 //   adamw_kernel     skip/clip prologue, fused AdamW, 16-bit write-back, INT8
-//   adamw_sched_kernel  the same (no INT8) for large shards: a persistent
-//                    grid taking groups of tiles from a counter in the state
+//   adamw_sched_kernel  the same for large shards: a persistent grid taking
+//                    groups of tiles from a counter in the state
 //   finalize_kernel  loss scaler and counters
 //   quant_kernel     INT8 of an existing 16-bit slot (quad tiles)
 //   quant8_kernel    the same on 16-byte aligned slots, eight elements per lane
@@ -80,7 +80,8 @@ constexpr int kMaxGridReduce = ZERO_MAX_PARTIALS;
 // INT8 quantiser and gather) ran 30-70% slower and keep full occupancy, and
 // so do launches of fewer than kTwoBlocksMin blocks (the 7B block's reduce,
 // 6,200 blocks, ran 1-2% slower with the cap) and the update with the INT8
-// epilogue (on the 70B shard 5.85 against 5.35 ms in slices without it).
+// epilogue when issued in slices (on the 70B shard 5.85 against 5.35 ms
+// without the cap; a shard that large now takes the counter-scheduled form).
 constexpr int64_t kSliceBlocks = 32768;
 constexpr unsigned kLdsTwoBlocks = 56 * 1024;
 constexpr int64_t kTwoBlocksMin = 8192;
