@@ -224,6 +224,7 @@ def test_adamw_group_counter_across_calls(zf):
         if skip:
             units[0]["g"][12345] = float("inf")
         before = [to_host(U["master"]).copy() for U in units] if skip else None
+        before_q = (to_host(units[1]["q"]).copy(), to_host(units[1]["qs"]).copy()) if skip else None
         for U in units:
             zf.zero_unscale_norm(U["g"], state)
         for u, U in enumerate(units):
@@ -236,6 +237,8 @@ def test_adamw_group_counter_across_calls(zf):
         if skip:
             for U, b in zip(units, before):
                 assert_bitwise(to_host(U["master"]), b, "master after a skipped step")
+            assert_bitwise(to_host(units[1]["q"]), before_q[0], "INT8 codes after a skipped step")
+            assert_bitwise(to_host(units[1]["qs"]), before_q[1], "INT8 scales after a skipped step")
             continue
         applied += 1
         gh = [to_host(U["g"]).copy() for U in units]
