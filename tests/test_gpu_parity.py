@@ -137,6 +137,11 @@ ADAM_CASES = [
     (1, 2, 1, 0, True, 1.0, 65536.0),
     (0, 1, 512, 512, True, 1e-3, 1.0),
     (2, 1, 65_536 + 255, 0, True, 0.5, 1.0),
+    # shards of 8,192 or more four-tile groups: the counter-scheduled update,
+    # with the INT8 epilogue, a ragged last tile, and the slot and the codes
+    # two elements off their vector boundaries (or aligned, clipping active)
+    (2, 2, 34_000_129, 6, True, 1.0, 1.0),
+    (1, 1, 34_000_001, 0, True, 1e-4, 65536.0),
 ]
 
 
